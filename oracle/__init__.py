@@ -1,0 +1,181 @@
+"""CPU oracle for the fused memory-bound kernels -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. The product path (the HIP library and
+its Python binding) never imports, links or calls it, and the two share no
+code: the oracle is plain C++ in double precision (``oracle.cpp``) built with
+g++, plus the pure-Python tiling model in ``tiling.py``.
+
+Arrays are numpy: fp32 as ``float32``, bf16 as ``uint16`` bit patterns.
+Every function cites the passage it follows in ``oracle.cpp``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from pathlib import Path
+
+import numpy as np
+
+from . import tiling  # noqa: F401  (re-exported)
+
+_HERE = Path(__file__).resolve().parent
+LIB_PATH = _HERE / "liboracle.so"
+
+OP_ADD_SCALAR = 1
+OP_MUL_SCALAR = 2
+OP_GELU_TANH = 3
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not LIB_PATH.exists():
+        from .build_oracle import build
+
+        build()
+    lib = ctypes.CDLL(str(LIB_PATH))
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+    sig = {
+        "oracle_f32_to_bf16": ([vp, vp, i64], None),
+        "oracle_bf16_to_f32": ([vp, vp, i64], None),
+        "oracle_gelu_tanh_f64": ([vp, vp, i64], None),
+        "oracle_gelu_tanh_literal_f64": ([vp, vp, i64], None),
+        "oracle_gelu_tanh_f32": ([vp, vp, i64, i32], None),
+        "oracle_gelu_tanh_bf16": ([vp, vp, i64, i32], None),
+        "oracle_chain_f32": ([vp, vp, i64, vp, vp, i32, i32], i32),
+        "oracle_chain_bf16": ([vp, vp, i64, vp, vp, i32, i32], i32),
+        "oracle_softmax_rows_f64": ([vp, vp, i64, i64, i64, i64], i32),
+        "oracle_softmax_rows_f32": ([vp, vp, i64, i64, i64, i64, i32], i32),
+        "oracle_softmax_rows_bf16": ([vp, vp, i64, i64, i64, i64, i32], i32),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def default_threads() -> int:
+    """Threads the oracle may use: the process's CPU share, capped by OMP_NUM_THREADS."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS")
+    if cap and cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _c(a: np.ndarray, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# ------------------------------------------------------------ rounding ----
+def f32_to_bf16(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns, round to nearest even, NaN kept (quiet)."""
+    x = _c(x, np.float32)
+    y = np.empty(x.shape, np.uint16)
+    _load().oracle_f32_to_bf16(_ptr(x), _ptr(y), x.size)
+    return y
+
+
+def bf16_to_f32(x: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> fp32 (exact widening)."""
+    x = _c(x, np.uint16)
+    y = np.empty(x.shape, np.float32)
+    _load().oracle_bf16_to_f32(_ptr(x), _ptr(y), x.size)
+    return y
+
+
+# ---------------------------------------------------------------- GELU ----
+def gelu_tanh_f64(x: np.ndarray) -> np.ndarray:
+    """The real tanh-GELU in double (cancellation-free form), unrounded."""
+    x = _c(x, np.float64)
+    y = np.empty_like(x)
+    _load().oracle_gelu_tanh_f64(_ptr(x), _ptr(y), x.size)
+    return y
+
+
+def gelu_tanh_literal_f64(x: np.ndarray) -> np.ndarray:
+    """The literal 0.5 x (1 + tanh u) in double, unrounded (for the pins)."""
+    x = _c(x, np.float64)
+    y = np.empty_like(x)
+    _load().oracle_gelu_tanh_literal_f64(_ptr(x), _ptr(y), x.size)
+    return y
+
+
+def gelu_tanh(x: np.ndarray, threads: int = 1) -> np.ndarray:
+    """tanh-GELU of fp32 (float32) or bf16 (uint16) data, same dtype out."""
+    lib = _load()
+    if x.dtype == np.uint16:
+        x = _c(x, np.uint16)
+        y = np.empty_like(x)
+        lib.oracle_gelu_tanh_bf16(_ptr(x), _ptr(y), x.size, threads)
+        return y
+    x = _c(x, np.float32)
+    y = np.empty_like(x)
+    lib.oracle_gelu_tanh_f32(_ptr(x), _ptr(y), x.size, threads)
+    return y
+
+
+# ---------------------------------------------------------------- chain ---
+def chain(x: np.ndarray, ops, threads: int = 1) -> np.ndarray:
+    """Apply ``ops`` ((kind, scalar) pairs, in order) elementwise, fp32 intermediates."""
+    kinds = np.array([k for k, _ in ops], np.int32)
+    scal = np.array([s for _, s in ops], np.float32)
+    lib = _load()
+    if x.dtype == np.uint16:
+        x = _c(x, np.uint16)
+        y = np.empty_like(x)
+        rc = lib.oracle_chain_bf16(_ptr(x), _ptr(y), x.size, _ptr(kinds), _ptr(scal), len(ops),
+                                   threads)
+    else:
+        x = _c(x, np.float32)
+        y = np.empty_like(x)
+        rc = lib.oracle_chain_f32(_ptr(x), _ptr(y), x.size, _ptr(kinds), _ptr(scal), len(ops),
+                                  threads)
+    if rc != 0:
+        raise ValueError(f"invalid op list {ops!r}")
+    return y
+
+
+# ---------------------------------------------------------------- softmax -
+def softmax_rows(x: np.ndarray, threads: int = 1, out: np.ndarray | None = None) -> np.ndarray:
+    """Softmax along the last axis of a 2-D array (float64, float32 or bf16 uint16).
+
+    Row strides of ``x`` (and of ``out`` if given) are honoured; entries of
+    ``out`` past ``cols`` in each row are left untouched.
+    """
+    if x.ndim != 2:
+        raise ValueError("softmax_rows expects a 2-D array")
+    rows, cols = x.shape
+    if x.strides[1] != x.itemsize:
+        x = np.ascontiguousarray(x)
+    if out is None:
+        out = np.empty((rows, cols), x.dtype)
+    if out.dtype != x.dtype or out.shape != x.shape or out.strides[1] != out.itemsize:
+        raise ValueError("out must match x in dtype and shape, unit column stride")
+    ldx = x.strides[0] // x.itemsize if rows > 1 else cols
+    ldy = out.strides[0] // out.itemsize if rows > 1 else cols
+    lib = _load()
+    if x.dtype == np.float64:
+        rc = lib.oracle_softmax_rows_f64(_ptr(x), _ptr(out), rows, cols, ldx, ldy)
+    elif x.dtype == np.float32:
+        rc = lib.oracle_softmax_rows_f32(_ptr(x), _ptr(out), rows, cols, ldx, ldy, threads)
+    elif x.dtype == np.uint16:
+        rc = lib.oracle_softmax_rows_bf16(_ptr(x), _ptr(out), rows, cols, ldx, ldy, threads)
+    else:
+        raise TypeError(f"unsupported dtype {x.dtype}")
+    if rc != 0:
+        raise ValueError("invalid softmax sizes")
+    return out
