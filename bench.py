@@ -1,0 +1,335 @@
+#!/usr/bin/env python3
+"""Achieved HBM bandwidth of the fused memory-bound kernels on one MI355X.
+
+One step = one pass of every kernel of the hot path over the large
+workloads, each with inputs resident in HBM:
+  C3   fused chain 0.5 * GELU(x + 1), fp32, 8,388,608 elements
+  C4   row softmax bf16, 32768 x 4096 (single-pass, rows on chip)
+  C5a  row softmax fp32, 1024 x 131072 (online two-pass, rows wider than chip)
+  C5b  tanh-GELU bf16, 2^30 elements
+Algorithmic bytes = one read + one write of every element ("Lecture 6: GPU
+Kernels and Triton", section 9.3: bandwidth utilisation = bytes moved /
+time / peak). ``value`` = total algorithmic bytes of the K timed steps /
+wall time between two device synchronisations, in GB/s (1e9 B/s).
+
+Per-kernel durations come from HIP events recorded on the launch stream
+around every launch of the timed steps. The CPU baseline runs the oracle
+once over the same step on the host's cores.
+
+Prints ONE JSON line. ``--gpus`` above 1 is refused: the build measures one
+GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+STEP = ("C3", "C4", "C5a", "C5b")
+TRAFFIC_FILE = ROOT / "profiles" / "traffic.json"
+KERNEL_SOURCES = ("device_common.hpp", "elementwise.hip", "softmax.hip")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        h.update((ROOT / "memory_bound_elementwise_fk_amd" / "csrc" / name).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timing (e.g. under a profiler)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the copy ceiling and the unfused-chain comparison")
+    return ap.parse_args()
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(every kernel here runs on one GPU's share of the data).", file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    from memory_bound_elementwise_fk_amd import LIB_PATH
+
+    if not LIB_PATH.exists():
+        import __graft_entry__
+
+        __graft_entry__.build()
+    import memory_bound_elementwise_fk_amd as fk
+    from memory_bound_elementwise_fk_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    # ---- inputs resident in HBM, outputs preallocated
+    log("generating inputs")
+    host = {name: wl.make_input(name) for name in STEP}
+    xs = {name: wl.to_torch(a, "cuda:0") for name, a in host.items()}
+    ys = {name: torch.empty_like(t) for name, t in xs.items()}
+    torch.cuda.synchronize()
+
+    launches = {
+        "C3": lambda: fk.fk_elementwise_chain(xs["C3"], ys["C3"], wl.CHAIN_C3),
+        "C4": lambda: fk.fk_softmax_rows(xs["C4"], ys["C4"]),
+        "C5a": lambda: fk.fk_softmax_rows(xs["C5a"], ys["C5a"]),
+        "C5b": lambda: fk.fk_gelu_tanh(xs["C5b"], ys["C5b"]),
+    }
+    kbytes = {name: wl.algorithmic_bytes(name) for name in STEP}
+    step_bytes = sum(kbytes.values())
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        for name in STEP:
+            launches[name]()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps between two synchronisations
+    ev = {name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(args.steps)] for name in STEP}
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        for name in STEP:
+            a, b = ev[name][k]
+            a.record(stream)
+            launches[name]()
+            b.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    per_kernel_ms = {name: sum(a.elapsed_time(b) for a, b in ev[name]) / args.steps
+                     for name in STEP}
+    value = step_bytes * args.steps / wall / 1e9
+    log(f"step {wall / args.steps * 1e3:.3f} ms, {value:.1f} GB/s")
+
+    kernels = {}
+    for name in STEP:
+        ms = per_kernel_ms[name]
+        gbs = kbytes[name] / (ms * 1e-3) / 1e9
+        kernels[name] = {"ms": round(ms, 5), "bytes": kbytes[name], "GBps": round(gbs, 1),
+                         "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
+
+    # ---- parity spot check of what was timed (full checks live in tests/)
+    spot = spot_check(host, ys, wl)
+    log(f"spot check: {spot}")
+
+    extras = {}
+    if not args.no_extras:
+        extras = measure_extras(fk, wl, torch, xs, ys, stream)
+
+    dominant = max(STEP, key=lambda n: per_kernel_ms[n])
+    achieved = kbytes[dominant] / (per_kernel_ms[dominant] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": traffic_bytes(dominant)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(host, kbytes)
+
+    result = {
+        "metric": "achieved HBM GB/s (% of ~8 TB/s peak) for fused GELU/chain and row softmax",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded PCG64 chunks; sizes and distributions of the five workloads)",
+        "config": {
+            "workload": "one step = C3 chain fp32 8,388,608 + C4 softmax bf16 32768x4096 + "
+                        "C5a softmax fp32 1024x131072 (online) + C5b tanh-GELU bf16 2^30",
+            "step_bytes": step_bytes,
+            "frac_of_peak": round(value / PEAK_HBM_GBS, 4),
+            "kernels": kernels,
+            "spot_check": spot,
+            **extras,
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+    return 0 if spot["ok"] else 1
+
+
+def spot_check(host, ys, wl):
+    """Compare a sample of every timed output with the oracle."""
+    import numpy as np
+
+    import oracle
+
+    rng = np.random.default_rng(1)
+    ok = True
+    worst = {}
+    # elementwise: 65536 random positions
+    for name in ("C3", "C5b"):
+        x = host[name]
+        idx = np.sort(rng.choice(x.size, 65536, replace=False))
+        got = wl.from_torch(ys[name])[idx]
+        if name == "C3":
+            ref = oracle.chain(x[idx], wl.CHAIN_C3)
+            rel = np.abs(got.astype(np.float64) - ref) / np.maximum(np.abs(ref), 1.2e-38)
+            worst[name] = float(rel.max())
+            ok &= worst[name] <= 1e-5
+        else:
+            ref = oracle.gelu_tanh(x[idx])
+            d = np.abs(_ord16(got) - _ord16(ref))
+            worst[name] = int(d.max())
+            ok &= worst[name] <= 1
+    # softmax: 16 random rows
+    for name in ("C4", "C5a"):
+        x = host[name]
+        rows = np.sort(rng.choice(x.shape[0], 16, replace=False))
+        got = wl.from_torch(ys[name][rows.tolist()])
+        ref = oracle.softmax_rows(np.ascontiguousarray(x[rows]))
+        if name == "C4":
+            worst[name] = int(np.abs(_ord16(got) - _ord16(ref)).max())
+            ok &= worst[name] <= 1
+        else:
+            worst[name] = float(np.abs(got.astype(np.float64) - ref).max())
+            ok &= worst[name] <= 2e-6
+    return {"ok": bool(ok), "worst": worst,
+            "tolerance": {"C3": "1e-5 rel", "C5b": "1 bf16 ulp", "C4": "1 bf16 ulp",
+                          "C5a": "2e-6 abs"}}
+
+
+def _ord16(bits):
+    import numpy as np
+
+    b = bits.astype(np.int32)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b)
+
+
+def measure_extras(fk, wl, torch, xs, ys, stream):
+    """Copy ceiling and fused-vs-unfused chain, outside the timed step."""
+    out = {}
+
+    def avg_ms(fn, reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        b.synchronize()
+        return a.elapsed_time(b) / reps
+
+    # plain 16-byte copy of the C5b tensor (2 GiB read + 2 GiB written)
+    nbytes = xs["C5b"].numel() * 2
+    ms = avg_ms(lambda: fk.fk_copy(xs["C5b"], ys["C5b"], nbytes), 10)
+    copy_gbs = 2 * nbytes / (ms * 1e-3) / 1e9
+    out["copy_ceiling"] = {"bytes": 2 * nbytes, "ms": round(ms, 4), "GBps": round(copy_gbs, 1),
+                           "frac_of_peak": round(copy_gbs / PEAK_HBM_GBS, 4)}
+
+    # C3 fused vs the same three ops as three kernels (fp32 intermediates).
+    # Each repetition first streams a 2 GiB copy so the 32 MiB operands are
+    # not served from the 256 MB Infinity Cache.
+    x = xs["C3"]
+    t1, t2, t3 = torch.empty_like(x), torch.empty_like(x), torch.empty_like(x)
+    ops = list(wl.CHAIN_C3)
+
+    def timed(fn, reps=20):
+        total = 0.0
+        for _ in range(reps):
+            fk.fk_copy(xs["C5b"], ys["C5b"], nbytes)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            total += a.elapsed_time(b)
+        return total / reps
+
+    fused_ms = timed(lambda: fk.fk_elementwise_chain(x, t3, ops))
+    unfused_ms = timed(lambda: (fk.fk_elementwise_chain(x, t1, ops[:1]),
+                                fk.fk_elementwise_chain(t1, t2, ops[1:2]),
+                                fk.fk_elementwise_chain(t2, t3, ops[2:])))
+    fb = wl.algorithmic_bytes("C3")
+    ub = wl.algorithmic_bytes("C3", unfused=True)
+    out["chain_fused_vs_unfused"] = {
+        "fused_ms": round(fused_ms, 5), "unfused_ms": round(unfused_ms, 5),
+        "fused_bytes": fb, "unfused_bytes": ub,
+        "fused_GBps": round(fb / (fused_ms * 1e-3) / 1e9, 1),
+        "unfused_GBps": round(ub / (unfused_ms * 1e-3) / 1e9, 1),
+        "speedup": round(unfused_ms / fused_ms, 3),
+        "pages_traffic_ratio": 3.0,
+        "note": "cold Infinity Cache before each measurement"}
+    return out
+
+
+def traffic_bytes(kernel: str):
+    """HBM bytes per launch of the dominant kernel from committed counter runs.
+
+    profiles/traffic.json holds FETCH_SIZE/WRITE_SIZE readings scaled by a
+    plain copy of known size; it is used only while the kernel sources are
+    unchanged since the counters were taken (same source hash).
+    """
+    if not TRAFFIC_FILE.exists():
+        return None
+    try:
+        rec = json.loads(TRAFFIC_FILE.read_text())
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    entry = rec.get("kernels", {}).get(kernel)
+    return None if entry is None else entry.get("bytes_per_launch")
+
+
+def cpu_baseline(host, kbytes):
+    """The oracle over one full step on the host cores (a bounded, ~seconds run)."""
+    import oracle
+    from memory_bound_elementwise_fk_amd import workloads as wl
+
+    threads = oracle.default_threads()
+    log(f"cpu baseline: oracle over one step on {threads} threads")
+    t0 = time.perf_counter()
+    oracle.chain(host["C3"], wl.CHAIN_C3, threads=threads)
+    oracle.softmax_rows(host["C4"], threads=threads)
+    oracle.softmax_rows(host["C5a"], threads=threads)
+    oracle.gelu_tanh(host["C5b"], threads=threads)
+    dt = time.perf_counter() - t0
+    total = sum(kbytes.values())
+    return {"value": round(total / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": "one full step (C3 + C4 + C5a + C5b, every element) through the "
+                      "double-precision C++ oracle, split over contiguous ranges/rows"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

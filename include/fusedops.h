@@ -1,0 +1,140 @@
+/*
+ * fusedops.h -- C ABI of libfusedops: fused memory-bound kernels for AMD
+ * Instinct MI355X (gfx950), each reading every element from HBM once and
+ * writing it once.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers: x and y are DEVICE pointers owned by the caller. The library
+ *   never allocates, frees or copies device memory and never synchronises.
+ *   Op lists (fk_op arrays) are HOST pointers, read before the call returns.
+ * Stream: a hipStream_t passed as void*; NULL is the null stream. Work is
+ *   enqueued on it and the call returns without waiting (launches are
+ *   asynchronous, as the profiling notes on the pages stress: the host runs
+ *   ahead of the device until it synchronises).
+ * dtype: FK_F32 (IEEE binary32) or FK_BF16 (bfloat16, the upper half of a
+ *   binary32). Input and output share the dtype. All arithmetic is fp32;
+ *   bf16 outputs are rounded to nearest, ties to even; NaN stays NaN.
+ * Sizes: element counts and strides are in ELEMENTS (not bytes), int64_t.
+ * Aliasing: y == x (exactly in place, and for row ops also ldy == ldx) is
+ *   allowed: every element is read before the same lane writes it. Any
+ *   other overlap of the input and output byte ranges is FK_ERR_OVERLAP.
+ * Alignment: any element-aligned pointer is accepted; 16-byte aligned data
+ *   takes the 128-bit vector path, other data a scalar path.
+ * Empty work (n == 0, rows == 0 or cols == 0) returns FK_OK and launches
+ *   nothing; pointers may then be NULL.
+ * Errors: invalid arguments return a negative fk_status BEFORE any HIP call
+ *   and nothing is launched. A failed launch returns FK_ERR_HIP.
+ * Threads: entry points keep no state and may be called concurrently.
+ */
+#ifndef FUSEDOPS_H
+#define FUSEDOPS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FK_F32 = 0, FK_BF16 = 1 } fk_dtype;
+
+typedef enum {
+    FK_OK = 0,
+    FK_ERR_INVALID_ARG = -1, /* null pointer with work to do, negative size,
+                                stride < cols, unknown dtype, bad op list   */
+    FK_ERR_UNSUPPORTED = -2, /* a size beyond what one launch can address   */
+    FK_ERR_OVERLAP = -3,     /* input and output overlap without being equal */
+    FK_ERR_HIP = -4          /* the HIP runtime reported an error           */
+} fk_status;
+
+/* Elementwise op kinds of a fused chain. */
+typedef enum {
+    FK_OP_ADD_SCALAR = 1, /* v = v + scalar               */
+    FK_OP_MUL_SCALAR = 2, /* v = v * scalar               */
+    FK_OP_GELU_TANH = 3   /* v = tanh-GELU(v); scalar ignored */
+} fk_op_kind;
+
+typedef struct {
+    int32_t kind;  /* an fk_op_kind */
+    float scalar;  /* operand of ADD / MUL */
+} fk_op;
+
+#define FK_MAX_OPS 8
+
+/*
+ * tanh-GELU, y[i] = 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))) for
+ * i in [0, n), as defined in the "CS336 lecture 6" notes (kyc001.github.io),
+ * section 4.2 "Case: GELU"; fused so that x is read once and y written once
+ * (section 4.1 of the same notes).
+ * Evaluated as the identical real function x / (1 + 2^t),
+ * t = x (A + B x^2), A = -2 sqrt(2/pi) log2(e), B = 0.044715 A, which does
+ * not cancel for negative x. Relative error <= 1e-5 for x >= -9 (fp32 out);
+ * GELU(+-0) = +-0, GELU(+inf) = +inf, GELU(-inf) = -0, GELU(NaN) = NaN.
+ * x, y: device arrays of n elements of dtype.
+ */
+int fk_gelu_tanh(const void* x, void* y, int64_t n, int dtype, void* stream);
+
+/*
+ * Fused elementwise chain: for every i in [0, n), v = x[i]; then each op of
+ * ops[0 .. n_ops) in order; y[i] = v. One HBM read and one write per
+ * element instead of one per op ("Lecture 6: GPU Kernels and Triton",
+ * cs336.sjfarmltd.com, section 1.1: three consecutive elementwise ops over
+ * 32 MB move 192 MB unfused and 64 MB fused). Every intermediate is
+ * rounded to fp32, so the fused result equals running each op as its own
+ * fp32 kernel (and is bitwise equal to it for ADD and MUL).
+ * ops: host array of n_ops in [1, FK_MAX_OPS] entries, copied by value into
+ * the launch. Unknown kinds are FK_ERR_INVALID_ARG.
+ */
+int fk_elementwise_chain(const void* x, void* y, int64_t n, int dtype,
+                         const fk_op* ops, int n_ops, void* stream);
+
+/*
+ * Row softmax: for each row r in [0, rows), with x_r = x + r*ldx and
+ * y_r = y + r*ldy: m = max_j x_r[j]; s = sum_j exp(x_r[j] - m);
+ * y_r[j] = exp(x_r[j] - m) / s for j in [0, cols) ("CS336 lecture 6" notes,
+ * section 5.2: one block per row, max, exponentials and their sum,
+ * normalise and write back). Entries past cols in a row (the stride
+ * padding) are neither read nor written. fp32 accumulation.
+ * Rows up to fk_softmax_onchip_max_cols(dtype) columns are held on chip
+ * (one read, one write per element); wider rows use the online max/sum
+ * two-pass of "Lecture 6: GPU Kernels and Triton", section 7.2.
+ * A row with NaN or +inf, or only -inf, comes out all NaN (the formula).
+ * ldx, ldy: row strides in elements, >= cols.
+ */
+int fk_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols,
+                    int64_t ldx, int64_t ldy, int dtype, void* stream);
+
+/*
+ * Same result as fk_softmax_rows, always through the wide-row online path:
+ * pass 1 streams the row and keeps a running max m and a running sum l,
+ * rescaling l by exp(m_old - m_new) whenever the max grows ("Lecture 6:
+ * GPU Kernels and Triton", section 7.2 "Online Softmax", without the
+ * attention accumulator); partial (m, l) pairs merge by the same rule;
+ * pass 2 re-reads the row and writes exp(x - m) / l. Any cols >= 1.
+ */
+int fk_softmax_rows_online(const void* x, void* y, int64_t rows, int64_t cols,
+                           int64_t ldx, int64_t ldy, int dtype, void* stream);
+
+/*
+ * Widest row (in columns) that fk_softmax_rows holds on chip for dtype, or
+ * FK_ERR_INVALID_ARG for an unknown dtype. Pure host query.
+ */
+int64_t fk_softmax_onchip_max_cols(int dtype);
+
+/*
+ * Byte copy y[0 .. nbytes) = x[0 .. nbytes), through the same 128-bit
+ * load/store path as the elementwise kernels: the bandwidth ceiling against
+ * which the kernels' achieved bytes / time is compared ("Lecture 6: GPU
+ * Kernels and Triton", section 9.3: bandwidth utilisation = bytes moved /
+ * time / peak). Overlapping ranges other than x == y are FK_ERR_OVERLAP.
+ */
+int fk_copy(const void* x, void* y, int64_t nbytes, void* stream);
+
+/* Static English text for an fk_status value (never NULL). */
+const char* fk_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FUSEDOPS_H */

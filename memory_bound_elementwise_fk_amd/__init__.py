@@ -1,0 +1,233 @@
+"""Python binding of libfusedops (fused memory-bound kernels for MI355X).
+
+Argument marshalling only: every function forwards torch device tensors'
+pointers, sizes and strides, plus the current HIP stream, to the C entry
+point of the same name in ``libfusedops.so`` (declared in
+``include/fusedops.h``); all computation happens in the HIP kernels. There
+is no fallback: without the built library every call raises.
+
+Tensors must live on a GPU device; torch is used only for device memory and
+streams. ``y`` is written in place (``y`` may be ``x`` itself).
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+LIB_PATH = Path(__file__).resolve().parent / "libfusedops.so"
+
+FK_F32 = 0
+FK_BF16 = 1
+FK_OK = 0
+FK_ERR_INVALID_ARG = -1
+FK_ERR_UNSUPPORTED = -2
+FK_ERR_OVERLAP = -3
+FK_ERR_HIP = -4
+FK_OP_ADD_SCALAR = 1
+FK_OP_MUL_SCALAR = 2
+FK_OP_GELU_TANH = 3
+FK_MAX_OPS = 8
+
+__all__ = [
+    "FusedOpsError", "lib", "fk_gelu_tanh", "fk_elementwise_chain", "fk_softmax_rows",
+    "fk_softmax_rows_online", "fk_softmax_onchip_max_cols", "fk_copy", "fk_status_string",
+    "gelu_tanh", "elementwise_chain", "softmax_rows",
+]
+
+
+class FusedOpsError(RuntimeError):
+    """A libfusedops entry point returned a negative fk_status."""
+
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {fk_status_string(status)} (status {status})")
+        self.status = status
+
+
+class fk_op(ctypes.Structure):  # noqa: N801  (C name)
+    _fields_ = [("kind", ctypes.c_int32), ("scalar", ctypes.c_float)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library with argument types set (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not LIB_PATH.exists():
+        raise RuntimeError(
+            f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
+    L = ctypes.CDLL(str(LIB_PATH))
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.fk_gelu_tanh.argtypes = [vp, vp, i64, i32, vp]
+    L.fk_gelu_tanh.restype = i32
+    L.fk_elementwise_chain.argtypes = [vp, vp, i64, i32, ctypes.POINTER(fk_op), i32, vp]
+    L.fk_elementwise_chain.restype = i32
+    for name in ("fk_softmax_rows", "fk_softmax_rows_online"):
+        fn = getattr(L, name)
+        fn.argtypes = [vp, vp, i64, i64, i64, i64, i32, vp]
+        fn.restype = i32
+    L.fk_softmax_onchip_max_cols.argtypes = [i32]
+    L.fk_softmax_onchip_max_cols.restype = i64
+    L.fk_copy.argtypes = [vp, vp, i64, vp]
+    L.fk_copy.restype = i32
+    L.fk_status_string.argtypes = [i32]
+    L.fk_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def fk_status_string(status: int) -> str:
+    return lib().fk_status_string(int(status)).decode()
+
+
+# ------------------------------------------------------------ marshalling -
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return FK_F32
+    if t.dtype == torch.bfloat16:
+        return FK_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _device_tensor(t, name: str):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor, got device {t.device}")
+
+
+def _stream_handle(t, stream) -> int | None:
+    if stream is None:
+        return _torch().cuda.current_stream(t.device).cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != FK_OK:
+        raise FusedOpsError(rc, what)
+
+
+def _flat_pair(x, y, what: str):
+    _device_tensor(x, "x")
+    _device_tensor(y, "y")
+    if x.dtype != y.dtype:
+        raise TypeError(f"{what}: x and y dtypes differ")
+    if x.numel() != y.numel():
+        raise ValueError(f"{what}: x has {x.numel()} elements, y {y.numel()}")
+    if x.device != y.device:
+        raise ValueError(f"{what}: x and y on different devices")
+    if not (x.is_contiguous() and y.is_contiguous()):
+        raise ValueError(f"{what}: x and y must be contiguous")
+    return x.numel(), _dtype_code(x)
+
+
+def _ops_array(ops):
+    ops = list(ops)
+    arr = (fk_op * max(1, len(ops)))()
+    for i, (kind, scalar) in enumerate(ops):
+        arr[i].kind = int(kind)
+        arr[i].scalar = float(scalar)
+    return arr, len(ops)
+
+
+def _rows_pair(x, y, what: str):
+    _device_tensor(x, "x")
+    _device_tensor(y, "y")
+    if x.dtype != y.dtype:
+        raise TypeError(f"{what}: x and y dtypes differ")
+    if x.dim() != 2 or y.dim() != 2 or tuple(x.shape) != tuple(y.shape):
+        raise ValueError(f"{what}: x and y must be 2-D of the same shape")
+    if x.device != y.device:
+        raise ValueError(f"{what}: x and y on different devices")
+    rows, cols = x.shape
+    if cols > 1 and (x.stride(1) != 1 or y.stride(1) != 1):
+        raise ValueError(f"{what}: rows must be contiguous (unit column stride)")
+    ldx = x.stride(0) if rows > 1 else cols
+    ldy = y.stride(0) if rows > 1 else cols
+    return rows, cols, ldx, ldy, _dtype_code(x)
+
+
+# -------------------------------------------------------- entry points ----
+def fk_gelu_tanh(x, y, stream=None) -> None:
+    """y = tanh-GELU(x) elementwise (fp32 or bf16, contiguous, same size)."""
+    n, dt = _flat_pair(x, y, "fk_gelu_tanh")
+    with _torch().cuda.device(x.device):
+        _check(lib().fk_gelu_tanh(x.data_ptr(), y.data_ptr(), n, dt, _stream_handle(x, stream)),
+               "fk_gelu_tanh")
+
+
+def fk_elementwise_chain(x, y, ops, stream=None) -> None:
+    """y = ops applied in order to x; ops is a sequence of (kind, scalar)."""
+    n, dt = _flat_pair(x, y, "fk_elementwise_chain")
+    arr, count = _ops_array(ops)
+    with _torch().cuda.device(x.device):
+        _check(lib().fk_elementwise_chain(x.data_ptr(), y.data_ptr(), n, dt, arr, count,
+                                          _stream_handle(x, stream)), "fk_elementwise_chain")
+
+
+def fk_softmax_rows(x, y, stream=None) -> None:
+    """Softmax along each row of a 2-D x into y (row strides honoured)."""
+    rows, cols, ldx, ldy, dt = _rows_pair(x, y, "fk_softmax_rows")
+    with _torch().cuda.device(x.device):
+        _check(lib().fk_softmax_rows(x.data_ptr(), y.data_ptr(), rows, cols, ldx, ldy, dt,
+                                     _stream_handle(x, stream)), "fk_softmax_rows")
+
+
+def fk_softmax_rows_online(x, y, stream=None) -> None:
+    """As fk_softmax_rows, always through the online two-pass kernel."""
+    rows, cols, ldx, ldy, dt = _rows_pair(x, y, "fk_softmax_rows_online")
+    with _torch().cuda.device(x.device):
+        _check(lib().fk_softmax_rows_online(x.data_ptr(), y.data_ptr(), rows, cols, ldx, ldy, dt,
+                                            _stream_handle(x, stream)), "fk_softmax_rows_online")
+
+
+def fk_softmax_onchip_max_cols(dtype) -> int:
+    """Widest row held on chip for a torch dtype or an FK_* code."""
+    code = dtype if isinstance(dtype, int) else (
+        FK_F32 if dtype == _torch().float32 else FK_BF16 if dtype == _torch().bfloat16 else -1)
+    v = lib().fk_softmax_onchip_max_cols(code)
+    if v < 0:
+        raise FusedOpsError(int(v), "fk_softmax_onchip_max_cols")
+    return int(v)
+
+
+def fk_copy(x, y, nbytes: int | None = None, stream=None) -> None:
+    """Copy nbytes (default: all of x) from x to y on the device."""
+    _device_tensor(x, "x")
+    _device_tensor(y, "y")
+    if nbytes is None:
+        nbytes = x.numel() * x.element_size()
+    if nbytes > x.numel() * x.element_size() or nbytes > y.numel() * y.element_size():
+        raise ValueError("fk_copy: nbytes exceeds a buffer")
+    with _torch().cuda.device(x.device):
+        _check(lib().fk_copy(x.data_ptr(), y.data_ptr(), nbytes, _stream_handle(x, stream)),
+               "fk_copy")
+
+
+# ---------------------------------------------- allocating conveniences --
+def gelu_tanh(x, stream=None):
+    y = _torch().empty_like(x, memory_format=_torch().contiguous_format)
+    fk_gelu_tanh(x, y, stream)
+    return y
+
+
+def elementwise_chain(x, ops, stream=None):
+    y = _torch().empty_like(x, memory_format=_torch().contiguous_format)
+    fk_elementwise_chain(x, y, ops, stream)
+    return y
+
+
+def softmax_rows(x, stream=None):
+    y = _torch().empty(x.shape, dtype=x.dtype, device=x.device)
+    fk_softmax_rows(x, y, stream)
+    return y

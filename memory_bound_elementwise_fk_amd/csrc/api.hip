@@ -1,0 +1,147 @@
+// api.hip -- the extern "C" entry points of libfusedops (declared and
+// documented in include/fusedops.h). Each validates its arguments on the
+// host, before any HIP call, then hands over to a launcher that enqueues one
+// kernel on the caller's stream and returns without synchronising.
+#include <limits>
+
+#include "fusedops.h"
+#include "launch.hpp"
+
+static_assert(FK_MAX_OPS == fk::kMaxOps, "op list size mismatch");
+static_assert(int(FK_OP_ADD_SCALAR) == int(fk::kOpAdd) && int(FK_OP_MUL_SCALAR) == int(fk::kOpMul) &&
+                  int(FK_OP_GELU_TANH) == int(fk::kOpGelu),
+              "op kind mismatch");
+static_assert(int(FK_F32) == int(fk::kF32) && int(FK_BF16) == int(fk::kBF16), "dtype mismatch");
+
+namespace {
+
+constexpr int64_t kI64Max = std::numeric_limits<int64_t>::max();
+
+bool dtype_ok(int dtype) { return dtype == FK_F32 || dtype == FK_BF16; }
+int64_t esize(int dtype) { return dtype == FK_F32 ? 4 : 2; }
+
+// Byte ranges [a, a + na) and [b, b + nb) intersect.
+bool ranges_overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a);
+    const uintptr_t pb = reinterpret_cast<uintptr_t>(b);
+    return pa < pb + static_cast<uintptr_t>(nb) && pb < pa + static_cast<uintptr_t>(na);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FK_OK : FK_ERR_HIP; }
+
+// Shared checks of the elementwise entry points; sets *nothing_to_do for n == 0.
+int check_flat(const void* x, const void* y, int64_t n, int64_t elem_bytes, bool* nothing_to_do) {
+    *nothing_to_do = false;
+    if (n < 0) return FK_ERR_INVALID_ARG;
+    if (n == 0) {
+        *nothing_to_do = true;
+        return FK_OK;
+    }
+    if (x == nullptr || y == nullptr) return FK_ERR_INVALID_ARG;
+    if (n > kI64Max / elem_bytes) return FK_ERR_UNSUPPORTED;
+    const int64_t bytes = n * elem_bytes;
+    if (x != y && ranges_overlap(x, bytes, y, bytes)) return FK_ERR_OVERLAP;
+    return FK_OK;
+}
+
+int check_rows(const void* x, const void* y, int64_t rows, int64_t cols, int64_t ldx,
+               int64_t ldy, int dtype, bool* nothing_to_do) {
+    *nothing_to_do = false;
+    if (!dtype_ok(dtype)) return FK_ERR_INVALID_ARG;
+    if (rows < 0 || cols < 0) return FK_ERR_INVALID_ARG;
+    if (rows == 0 || cols == 0) {
+        *nothing_to_do = true;
+        return FK_OK;
+    }
+    if (x == nullptr || y == nullptr) return FK_ERR_INVALID_ARG;
+    if (ldx < cols || ldy < cols) return FK_ERR_INVALID_ARG;
+    const int64_t es = esize(dtype);
+    // extent in elements of each operand: (rows - 1) * ld + cols, in bytes
+    if (rows - 1 > (kI64Max / es - cols) / ldx || rows - 1 > (kI64Max / es - cols) / ldy)
+        return FK_ERR_UNSUPPORTED;
+    const int64_t bx = ((rows - 1) * ldx + cols) * es;
+    const int64_t by = ((rows - 1) * ldy + cols) * es;
+    if (x == y) {
+        if (ldx != ldy) return FK_ERR_OVERLAP;
+    } else if (ranges_overlap(x, bx, y, by)) {
+        return FK_ERR_OVERLAP;
+    }
+    return FK_OK;
+}
+
+int softmax_entry(const void* x, void* y, int64_t rows, int64_t cols, int64_t ldx, int64_t ldy,
+                  int dtype, bool online, void* stream) {
+    bool skip = false;
+    const int st = check_rows(x, y, rows, cols, ldx, ldy, dtype, &skip);
+    if (st != FK_OK || skip) return st;
+    return hip_status(fk::launch_softmax(x, y, rows, cols, ldx, ldy, static_cast<fk::Dtype>(dtype),
+                                         online, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int fk_gelu_tanh(const void* x, void* y, int64_t n, int dtype, void* stream) {
+    if (!dtype_ok(dtype)) return FK_ERR_INVALID_ARG;
+    bool skip = false;
+    const int st = check_flat(x, y, n, esize(dtype), &skip);
+    if (st != FK_OK || skip) return st;
+    return hip_status(
+        fk::launch_gelu(x, y, n, static_cast<fk::Dtype>(dtype), static_cast<hipStream_t>(stream)));
+}
+
+int fk_elementwise_chain(const void* x, void* y, int64_t n, int dtype, const fk_op* ops,
+                         int n_ops, void* stream) {
+    if (!dtype_ok(dtype)) return FK_ERR_INVALID_ARG;
+    if (ops == nullptr || n_ops < 1 || n_ops > FK_MAX_OPS) return FK_ERR_INVALID_ARG;
+    fk::OpList list{};
+    list.n = n_ops;
+    for (int i = 0; i < n_ops; ++i) {
+        const int32_t k = ops[i].kind;
+        if (k != FK_OP_ADD_SCALAR && k != FK_OP_MUL_SCALAR && k != FK_OP_GELU_TANH)
+            return FK_ERR_INVALID_ARG;
+        list.kind[i] = k;
+        list.scalar[i] = ops[i].scalar;
+    }
+    bool skip = false;
+    const int st = check_flat(x, y, n, esize(dtype), &skip);
+    if (st != FK_OK || skip) return st;
+    return hip_status(fk::launch_chain(x, y, n, static_cast<fk::Dtype>(dtype), list,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int fk_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols, int64_t ldx, int64_t ldy,
+                    int dtype, void* stream) {
+    return softmax_entry(x, y, rows, cols, ldx, ldy, dtype, false, stream);
+}
+
+int fk_softmax_rows_online(const void* x, void* y, int64_t rows, int64_t cols, int64_t ldx,
+                           int64_t ldy, int dtype, void* stream) {
+    return softmax_entry(x, y, rows, cols, ldx, ldy, dtype, true, stream);
+}
+
+int64_t fk_softmax_onchip_max_cols(int dtype) {
+    if (!dtype_ok(dtype)) return FK_ERR_INVALID_ARG;
+    return fk::softmax_onchip_max_cols(static_cast<fk::Dtype>(dtype));
+}
+
+int fk_copy(const void* x, void* y, int64_t nbytes, void* stream) {
+    bool skip = false;
+    const int st = check_flat(x, y, nbytes, 1, &skip);
+    if (st != FK_OK || skip) return st;
+    return hip_status(fk::launch_copy(x, y, nbytes, static_cast<hipStream_t>(stream)));
+}
+
+const char* fk_status_string(int status) {
+    switch (status) {
+        case FK_OK: return "ok";
+        case FK_ERR_INVALID_ARG: return "invalid argument";
+        case FK_ERR_UNSUPPORTED: return "unsupported size";
+        case FK_ERR_OVERLAP: return "input and output overlap without being equal";
+        case FK_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"
