@@ -35,7 +35,17 @@ sys.path.insert(0, str(ROOT))
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
 STEP = ("C3", "C4", "C5a", "C5b")
 TRAFFIC_FILE = ROOT / "profiles" / "traffic.json"
-KERNEL_SOURCES = ("device_common.hpp", "elementwise.hip", "softmax.hip")
+KERNEL_SOURCES = ("device_common.hpp", "ew_kernels.hpp", "softmax_kernels.hpp", "elementwise.hip",
+                  "softmax.hip")
+# Kernel-name fragments (as rocprofv3 prints them) of each workload's kernel.
+KERNEL_NAMES = {
+    "C3": ("ew_vec_kernel<fk::IoF32", "ChainOp"),
+    "C4": ("softmax_reg_kernel<fk::IoBF16",),
+    "C5a": ("softmax_split_kernel<fk::IoF32",),
+    "C5b": ("ew_vec_kernel<fk::IoBF16", "GeluOp"),
+    "copy": ("copy_vec_kernel",),
+}
+CPU_BASELINE_MIN_SECONDS = 10.0
 
 
 def kernel_source_hash() -> str:
@@ -58,11 +68,19 @@ def parse():
                     help="skip the oracle timing (e.g. under a profiler)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the copy ceiling and the unfused-chain comparison")
+    ap.add_argument("--counters-run", action="store_true",
+                    help="launch each kernel of the step twice plus a 1 GiB calibration copy, "
+                         "nothing else (for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE passes)")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn the two rocprofv3 counter_collection.csv files of a "
+                         "--counters-run into profiles/traffic.json and exit")
     return ap.parse_args()
 
 
 def main() -> int:
     args = parse()
+    if args.ingest_counters:
+        return ingest_counters(*args.ingest_counters)
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(every kernel here runs on one GPU's share of the data).", file=sys.stderr)
@@ -97,12 +115,18 @@ def main() -> int:
     ys = {name: torch.empty_like(t) for name, t in xs.items()}
     torch.cuda.synchronize()
 
+    # C5a rows are wider than one workgroup: the split path exchanges partial
+    # statistics through a zeroed workspace, allocated here once (untimed)
+    ws_bytes = fk.fk_softmax_workspace_bytes(*xs["C5a"].shape, xs["C5a"].dtype)
+    ws = torch.zeros(max(ws_bytes, 8), dtype=torch.uint8, device=dev)
     launches = {
         "C3": lambda: fk.fk_elementwise_chain(xs["C3"], ys["C3"], wl.CHAIN_C3),
         "C4": lambda: fk.fk_softmax_rows(xs["C4"], ys["C4"]),
-        "C5a": lambda: fk.fk_softmax_rows(xs["C5a"], ys["C5a"]),
+        "C5a": lambda: fk.fk_softmax_rows_ws(xs["C5a"], ys["C5a"], ws),
         "C5b": lambda: fk.fk_gelu_tanh(xs["C5b"], ys["C5b"]),
     }
+    if args.counters_run:
+        return counters_run(fk, torch, launches, xs, ys)
     kbytes = {name: wl.algorithmic_bytes(name) for name in STEP}
     step_bytes = sum(kbytes.values())
 
@@ -312,23 +336,107 @@ def traffic_bytes(kernel: str):
 
 
 def cpu_baseline(host, kbytes):
-    """The oracle over one full step on the host cores (a bounded, ~seconds run)."""
+    """The oracle over whole steps on the host cores, repeated for >= 10 s."""
     import oracle
     from memory_bound_elementwise_fk_amd import workloads as wl
 
     threads = oracle.default_threads()
-    log(f"cpu baseline: oracle over one step on {threads} threads")
+    log(f"cpu baseline: oracle over whole steps on {threads} threads")
+    reps = 0
     t0 = time.perf_counter()
-    oracle.chain(host["C3"], wl.CHAIN_C3, threads=threads)
-    oracle.softmax_rows(host["C4"], threads=threads)
-    oracle.softmax_rows(host["C5a"], threads=threads)
-    oracle.gelu_tanh(host["C5b"], threads=threads)
-    dt = time.perf_counter() - t0
-    total = sum(kbytes.values())
+    while True:
+        oracle.chain(host["C3"], wl.CHAIN_C3, threads=threads)
+        oracle.softmax_rows(host["C4"], threads=threads)
+        oracle.softmax_rows(host["C5a"], threads=threads)
+        oracle.gelu_tanh(host["C5b"], threads=threads)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= CPU_BASELINE_MIN_SECONDS:
+            break
+    total = sum(kbytes.values()) * reps
     return {"value": round(total / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
-            "kind": "oracle", "seconds": round(dt, 3),
-            "sample": "one full step (C3 + C4 + C5a + C5b, every element) through the "
+            "kind": "oracle", "seconds": round(dt, 3), "steps": reps,
+            "sample": f"{reps} full steps (C3 + C4 + C5a + C5b, every element) through the "
                       "double-precision C++ oracle, split over contiguous ranges/rows"}
+
+
+def counters_run(fk, torch, launches, xs, ys):
+    """Each step kernel twice and one 1 GiB copy, for per-dispatch counters."""
+    calib = 1 << 30
+    a = torch.empty(calib, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    fk.fk_copy(a, b, calib)
+    for _ in range(2):
+        for name in STEP:
+            launches[name]()
+    torch.cuda.synchronize()
+    log(f"counters run done: calibration copy {calib} B, then 2 x {', '.join(STEP)}")
+    return 0
+
+
+def _read_counter_csv(path):
+    """{(dispatch_id, kernel_name): value} of the one counter a rocprofv3 CSV holds."""
+    import csv
+
+    out, names = {}, set()
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            names.add(row["Counter_Name"])
+            key = (int(row["Dispatch_Id"]), row["Kernel_Name"])
+            out[key] = out.get(key, 0.0) + float(row["Counter_Value"])
+    if len(names) != 1:
+        raise SystemExit(f"{path}: expected one counter, found {sorted(names)}")
+    return names.pop(), out
+
+
+def _match(kernel_name: str, frags) -> bool:
+    return all(f in kernel_name for f in frags)
+
+
+def ingest_counters(fetch_csv: str, write_csv: str) -> int:
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of a --counters-run -> traffic.json.
+
+    Each counter is scaled by what it reads for the calibration copy, whose
+    true traffic is known (1 GiB read and 1 GiB written), so the figures are
+    HBM-side bytes per launch of each kernel.
+    """
+    from memory_bound_elementwise_fk_amd import workloads as wl
+
+    fname, fetch = _read_counter_csv(fetch_csv)
+    wname, write = _read_counter_csv(write_csv)
+    if fname != "FETCH_SIZE" or wname != "WRITE_SIZE":
+        raise SystemExit(f"expected FETCH_SIZE then WRITE_SIZE, got {fname}, {wname}")
+    calib = float(1 << 30)
+
+    def per_kernel(table, frags):
+        vals = [v for (d, k), v in sorted(table.items()) if _match(k, frags)]
+        return vals
+
+    cf, cw = per_kernel(fetch, KERNEL_NAMES["copy"]), per_kernel(write, KERNEL_NAMES["copy"])
+    if not cf or not cw:
+        raise SystemExit("calibration copy not found in the counter files")
+    f_scale = calib / (cf[0] * 1024.0)
+    w_scale = calib / (cw[0] * 1024.0)
+    rec = {"source_hash": kernel_source_hash(),
+           "calibration": {"bytes_each_way": int(calib), "fetch_kib": cf[0], "write_kib": cw[0],
+                           "fetch_scale": f_scale, "write_scale": w_scale},
+           "kernels": {}}
+    for name in STEP:
+        fv = per_kernel(fetch, KERNEL_NAMES[name])
+        wv = per_kernel(write, KERNEL_NAMES[name])
+        if not fv or not wv:
+            raise SystemExit(f"kernel of {name} not found in the counter files")
+        fb = sum(fv) / len(fv) * 1024.0 * f_scale
+        wb = sum(wv) / len(wv) * 1024.0 * w_scale
+        alg = wl.algorithmic_bytes(name)
+        rec["kernels"][name] = {"fetch_bytes": round(fb), "write_bytes": round(wb),
+                                "bytes_per_launch": round(fb + wb), "algorithmic_bytes": alg,
+                                "ratio_to_algorithmic": round((fb + wb) / alg, 4),
+                                "dispatches": len(fv)}
+    TRAFFIC_FILE.parent.mkdir(exist_ok=True)
+    TRAFFIC_FILE.write_text(json.dumps(rec, indent=2) + "\n")
+    print(json.dumps(rec, indent=2))
+    return 0
 
 
 if __name__ == "__main__":

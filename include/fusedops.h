@@ -6,8 +6,11 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * Pointers: x and y are DEVICE pointers owned by the caller. The library
- *   never allocates, frees or copies device memory and never synchronises.
- *   Op lists (fk_op arrays) are HOST pointers, read before the call returns.
+ *   never synchronises and never copies device memory; the only memory it
+ *   allocates is the small stream-ordered workspace of fk_softmax_rows on
+ *   rows wider than on-chip capacity (fk_softmax_rows_ws takes it from the
+ *   caller instead). Op lists (fk_op arrays) are HOST pointers, read before
+ *   the call returns.
  * Stream: a hipStream_t passed as void*; NULL is the null stream. Work is
  *   enqueued on it and the call returns without waiting (launches are
  *   asynchronous, as the profiling notes on the pages stress: the host runs
@@ -95,14 +98,58 @@ int fk_elementwise_chain(const void* x, void* y, int64_t n, int dtype,
  * section 5.2: one block per row, max, exponentials and their sum,
  * normalise and write back). Entries past cols in a row (the stride
  * padding) are neither read nor written. fp32 accumulation.
- * Rows up to fk_softmax_onchip_max_cols(dtype) columns are held on chip
- * (one read, one write per element); wider rows use the online max/sum
- * two-pass of "Lecture 6: GPU Kernels and Triton", section 7.2.
+ * Every path reads each element from HBM once and writes it once, except
+ * the online fallback:
+ *  - rows up to fk_softmax_onchip_max_cols(dtype) columns: one workgroup
+ *    (or one wave) per row, the row held in registers;
+ *  - wider rows, up to 64 slices of 8192 columns: the row is split over
+ *    several workgroups that each hold one slice in registers and exchange
+ *    partial (max, sum) pairs through a workspace, merged with the online
+ *    softmax rule of "Lecture 6: GPU Kernels and Triton", section 7.2;
+ *    fk_softmax_rows allocates that workspace itself (hipMallocAsync,
+ *    zeroed by a kernel, hipFreeAsync, all on `stream`);
+ *  - otherwise (or if that allocation fails): the online two-pass kernel
+ *    (see fk_softmax_rows_online), which reads the row twice.
  * A row with NaN or +inf, or only -inf, comes out all NaN (the formula).
  * ldx, ldy: row strides in elements, >= cols.
  */
 int fk_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols,
                     int64_t ldx, int64_t ldy, int dtype, void* stream);
+
+/*
+ * fk_softmax_rows with a caller-owned workspace for the split path; the
+ * library then allocates nothing. workspace: DEVICE memory of at least
+ * fk_softmax_workspace_bytes(rows, cols, dtype) bytes, 8-byte aligned,
+ * all zero before its first use; every completed call leaves it all zero
+ * again, so it is zeroed once and reused. Calls that share a workspace must
+ * not run concurrently (order them on one stream). When that size is 0 the
+ * workspace is ignored and may be NULL. Errors: FK_ERR_INVALID_ARG for a
+ * missing, misaligned or too small workspace or workspace_bytes < 0;
+ * FK_ERR_OVERLAP if it overlaps x or y.
+ */
+int fk_softmax_rows_ws(const void* x, void* y, int64_t rows, int64_t cols,
+                       int64_t ldx, int64_t ldy, int dtype, void* workspace,
+                       int64_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of zeroed workspace the split path needs for rows x cols of dtype:
+ * rows * slices * 8 + rows * 4 (rounded up to 8), with
+ * slices = ceil(cols / 8192); 0 when the rows fit on chip or the split path
+ * does not apply. FK_ERR_INVALID_ARG for negative sizes or an unknown
+ * dtype. Pure host query.
+ */
+int64_t fk_softmax_workspace_bytes(int64_t rows, int64_t cols, int dtype);
+
+/*
+ * Bound on the polls (each followed by a short sleep) that a split-path
+ * workgroup spends waiting for the other slices of its row. Past it the
+ * workgroup computes the row's max and sum by streaming the whole row
+ * itself, so the kernel ends and stays correct whatever the scheduling.
+ * Default 2^20. Returns the previous bound, or FK_ERR_INVALID_ARG for
+ * polls < 0. Process-wide; for tests and diagnostics (0 forces every
+ * split workgroup onto the streamed statistics).
+ */
+int64_t fk_set_split_wait_limit(int64_t polls);
 
 /*
  * Same result as fk_softmax_rows, always through the wide-row online path:

@@ -30,7 +30,8 @@ FK_MAX_OPS = 8
 
 __all__ = [
     "FusedOpsError", "lib", "fk_gelu_tanh", "fk_elementwise_chain", "fk_softmax_rows",
-    "fk_softmax_rows_online", "fk_softmax_onchip_max_cols", "fk_copy", "fk_status_string",
+    "fk_softmax_rows_online", "fk_softmax_rows_ws", "fk_softmax_workspace_bytes",
+    "fk_set_split_wait_limit", "fk_softmax_onchip_max_cols", "fk_copy", "fk_status_string",
     "gelu_tanh", "elementwise_chain", "softmax_rows",
 ]
 
@@ -68,6 +69,12 @@ def lib() -> ctypes.CDLL:
         fn = getattr(L, name)
         fn.argtypes = [vp, vp, i64, i64, i64, i64, i32, vp]
         fn.restype = i32
+    L.fk_softmax_rows_ws.argtypes = [vp, vp, i64, i64, i64, i64, i32, vp, i64, vp]
+    L.fk_softmax_rows_ws.restype = i32
+    L.fk_softmax_workspace_bytes.argtypes = [i64, i64, i32]
+    L.fk_softmax_workspace_bytes.restype = i64
+    L.fk_set_split_wait_limit.argtypes = [i64]
+    L.fk_set_split_wait_limit.restype = i64
     L.fk_softmax_onchip_max_cols.argtypes = [i32]
     L.fk_softmax_onchip_max_cols.restype = i64
     L.fk_copy.argtypes = [vp, vp, i64, vp]
@@ -191,11 +198,47 @@ def fk_softmax_rows_online(x, y, stream=None) -> None:
                                             _stream_handle(x, stream)), "fk_softmax_rows_online")
 
 
+def fk_softmax_rows_ws(x, y, workspace, stream=None) -> None:
+    """As fk_softmax_rows with a caller-owned workspace (a zeroed device
+    tensor of at least fk_softmax_workspace_bytes bytes; None when that is 0)."""
+    rows, cols, ldx, ldy, dt = _rows_pair(x, y, "fk_softmax_rows_ws")
+    if workspace is None:
+        wptr, wbytes = None, 0
+    else:
+        _device_tensor(workspace, "workspace")
+        wptr, wbytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    with _torch().cuda.device(x.device):
+        _check(lib().fk_softmax_rows_ws(x.data_ptr(), y.data_ptr(), rows, cols, ldx, ldy, dt,
+                                        wptr, wbytes, _stream_handle(x, stream)),
+               "fk_softmax_rows_ws")
+
+
+def _dtype_arg(dtype) -> int:
+    if isinstance(dtype, int):
+        return dtype
+    torch = _torch()
+    return FK_F32 if dtype == torch.float32 else FK_BF16 if dtype == torch.bfloat16 else -1
+
+
+def fk_softmax_workspace_bytes(rows: int, cols: int, dtype) -> int:
+    """Zeroed workspace bytes fk_softmax_rows_ws needs (0: none)."""
+    v = lib().fk_softmax_workspace_bytes(int(rows), int(cols), _dtype_arg(dtype))
+    if v < 0:
+        raise FusedOpsError(int(v), "fk_softmax_workspace_bytes")
+    return int(v)
+
+
+def fk_set_split_wait_limit(polls: int) -> int:
+    """Set the split path's bound on waiting polls; returns the previous bound."""
+    v = lib().fk_set_split_wait_limit(int(polls))
+    if v < 0:
+        raise FusedOpsError(int(v), "fk_set_split_wait_limit")
+    return int(v)
+
+
 def fk_softmax_onchip_max_cols(dtype) -> int:
     """Widest row held on chip for a torch dtype or an FK_* code."""
-    code = dtype if isinstance(dtype, int) else (
-        FK_F32 if dtype == _torch().float32 else FK_BF16 if dtype == _torch().bfloat16 else -1)
-    v = lib().fk_softmax_onchip_max_cols(code)
+    v = lib().fk_softmax_onchip_max_cols(_dtype_arg(dtype))
     if v < 0:
         raise FusedOpsError(int(v), "fk_softmax_onchip_max_cols")
     return int(v)

@@ -69,13 +69,32 @@ int check_rows(const void* x, const void* y, int64_t rows, int64_t cols, int64_t
     return FK_OK;
 }
 
-int softmax_entry(const void* x, void* y, int64_t rows, int64_t cols, int64_t ldx, int64_t ldy,
-                  int dtype, bool online, void* stream) {
-    bool skip = false;
-    const int st = check_rows(x, y, rows, cols, ldx, ldy, dtype, &skip);
-    if (st != FK_OK || skip) return st;
+int softmax_launch(const void* x, void* y, int64_t rows, int64_t cols, int64_t ldx, int64_t ldy,
+                   int dtype, bool online, void* ws, int64_t ws_bytes, void* stream) {
     return hip_status(fk::launch_softmax(x, y, rows, cols, ldx, ldy, static_cast<fk::Dtype>(dtype),
-                                         online, static_cast<hipStream_t>(stream)));
+                                         online, ws, ws_bytes, static_cast<hipStream_t>(stream)));
+}
+
+// Rows wider than on-chip capacity take the split path with a workspace the
+// call allocates, zeroes and frees in stream order; if the allocation fails
+// the online two-pass path runs instead.
+int softmax_self_managed(const void* x, void* y, int64_t rows, int64_t cols, int64_t ldx,
+                         int64_t ldy, int dtype, void* stream) {
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t need = fk::softmax_workspace_bytes(rows, cols, static_cast<fk::Dtype>(dtype));
+    if (need > 0) {
+        void* ws = nullptr;
+        if (hipMallocAsync(&ws, static_cast<size_t>(need), s) == hipSuccess) {
+            hipError_t e = fk::launch_zero_fill(ws, need, s);
+            if (e == hipSuccess)
+                e = fk::launch_softmax(x, y, rows, cols, ldx, ldy, static_cast<fk::Dtype>(dtype),
+                                       false, ws, need, s);
+            const hipError_t f = hipFreeAsync(ws, s);
+            return hip_status(e != hipSuccess ? e : f);
+        }
+        (void)hipGetLastError();  // clear the failed allocation; use the online path
+    }
+    return softmax_launch(x, y, rows, cols, ldx, ldy, dtype, false, nullptr, 0, stream);
 }
 
 }  // namespace
@@ -113,12 +132,50 @@ int fk_elementwise_chain(const void* x, void* y, int64_t n, int dtype, const fk_
 
 int fk_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols, int64_t ldx, int64_t ldy,
                     int dtype, void* stream) {
-    return softmax_entry(x, y, rows, cols, ldx, ldy, dtype, false, stream);
+    bool skip = false;
+    const int st = check_rows(x, y, rows, cols, ldx, ldy, dtype, &skip);
+    if (st != FK_OK || skip) return st;
+    return softmax_self_managed(x, y, rows, cols, ldx, ldy, dtype, stream);
+}
+
+int fk_softmax_rows_ws(const void* x, void* y, int64_t rows, int64_t cols, int64_t ldx,
+                       int64_t ldy, int dtype, void* workspace, int64_t workspace_bytes,
+                       void* stream) {
+    bool skip = false;
+    int st = check_rows(x, y, rows, cols, ldx, ldy, dtype, &skip);
+    if (st != FK_OK) return st;
+    if (workspace_bytes < 0) return FK_ERR_INVALID_ARG;
+    if (skip) return FK_OK;
+    const int64_t need = fk::softmax_workspace_bytes(rows, cols, static_cast<fk::Dtype>(dtype));
+    if (need > 0) {
+        if (workspace == nullptr || workspace_bytes < need) return FK_ERR_INVALID_ARG;
+        if ((reinterpret_cast<uintptr_t>(workspace) & 7u) != 0) return FK_ERR_INVALID_ARG;
+        const int64_t es = esize(dtype);
+        if (ranges_overlap(workspace, need, x, ((rows - 1) * ldx + cols) * es) ||
+            ranges_overlap(workspace, need, y, ((rows - 1) * ldy + cols) * es))
+            return FK_ERR_OVERLAP;
+    }
+    return softmax_launch(x, y, rows, cols, ldx, ldy, dtype, false, need > 0 ? workspace : nullptr,
+                          need, stream);
+}
+
+int64_t fk_softmax_workspace_bytes(int64_t rows, int64_t cols, int dtype) {
+    if (!dtype_ok(dtype) || rows < 0 || cols < 0) return FK_ERR_INVALID_ARG;
+    if (rows == 0 || cols == 0) return 0;
+    return fk::softmax_workspace_bytes(rows, cols, static_cast<fk::Dtype>(dtype));
+}
+
+int64_t fk_set_split_wait_limit(int64_t polls) {
+    if (polls < 0) return FK_ERR_INVALID_ARG;
+    return fk::set_split_wait_limit(polls);
 }
 
 int fk_softmax_rows_online(const void* x, void* y, int64_t rows, int64_t cols, int64_t ldx,
                            int64_t ldy, int dtype, void* stream) {
-    return softmax_entry(x, y, rows, cols, ldx, ldy, dtype, true, stream);
+    bool skip = false;
+    const int st = check_rows(x, y, rows, cols, ldx, ldy, dtype, &skip);
+    if (st != FK_OK || skip) return st;
+    return softmax_launch(x, y, rows, cols, ldx, ldy, dtype, true, nullptr, 0, stream);
 }
 
 int64_t fk_softmax_onchip_max_cols(int dtype) {

@@ -91,13 +91,24 @@ __device__ inline void st16(u32x4* p, u32x4 v) {
 // ---------------------------------------------------------------- math ---
 constexpr float kLog2e = 1.4426950408889634f;
 
-// 2^a for any a, including results below 2^-126: the hardware exp2
-// (v_exp_f32) does not return subnormals, so such results are formed as
-// 2^(a+32) * 2^-32, whose final multiply rounds to the subnormal.
-__device__ inline float exp2_full(float a) {
-    float e = __builtin_amdgcn_exp2f(a);
-    if (a < -126.0f) e = __builtin_amdgcn_exp2f(a + 32.0f) * 0x1p-32f;
-    return e;
+// Raw hardware 2^a (v_exp_f32). Results below 2^-126 come back as zero, which
+// is harmless where they only feed a sum that is at least 1.
+__device__ inline float exp2_raw(float a) { return __builtin_amdgcn_exp2f(a); }
+
+// Softmax numerators are computed as e' = 2^(a + kSoftmaxBias), a = (x - m)
+// log2(e) <= 0, and normalised by the sum of the same e'; the common factor
+// 2^kSoftmaxBias cancels exactly (a power of two). The bias keeps e' normal
+// down to a = -134: any smaller numerator gives an output below 2^-134,
+// which is zero in bf16 (half its smallest subnormal, a tie to even) and
+// below 5e-41 in fp32. The bias costs at most 2^-22 of rounding on the
+// exponent argument (its magnitude stays below 8 for the numerators that
+// matter), i.e. <= 1.7e-7 relative on e'.
+constexpr float kSoftmaxBias = 8.0f;
+constexpr float kSoftmaxScale = 256.0f;  // 2^kSoftmaxBias
+
+// e' for one element: one subtraction, one fused multiply-add, one exp.
+__device__ inline float softmax_numerator(float x, float m) {
+    return exp2_raw(fmaf(x - m, kLog2e, kSoftmaxBias));
 }
 
 // tanh-GELU: 0.5 x (1 + tanh u), u = sqrt(2/pi) (x + 0.044715 x^3)
@@ -108,19 +119,41 @@ __device__ inline float exp2_full(float a) {
 // negative x (the literal form loses all digits below x ~ -3 in fp32).
 constexpr float kGeluA = -2.302208198144325f;    // -2 * sqrt(2/pi) * log2(e)
 constexpr float kGeluB = -0.10294323958002348f;  // 0.044715 * kGeluA
+// Above this t (x below ~ -9.5) 1 + 2^t is 2^t to fp32 precision and its
+// reciprocal would leave the normal range; those lanes take the far path.
+constexpr float kGeluFarT = 120.0f;
 
-// x far below zero (t > 120, i.e. x < ~ -9.5): 1 + 2^t rounds to 2^t, so the
-// result is x * 2^-t; the scale is split so that no factor is subnormal.
-__device__ __noinline__ float gelu_far_negative(float x, float t) {
-    if (x == -__builtin_inff()) return -0.0f;  // the limit at -inf
-    return (x * __builtin_amdgcn_exp2f(64.0f - t)) * 0x1p-64f;
+__device__ inline float gelu_t(float x) { return x * fmaf(kGeluB, x * x, kGeluA); }
+
+// x * 2^-t, scaled so that no intermediate is subnormal; the limit -0 at -inf.
+__device__ inline float gelu_far(float x, float t) {
+    const float y = (x * exp2_raw(64.0f - t)) * 0x1p-64f;
+    return x == -__builtin_inff() ? -0.0f : y;
 }
 
-__device__ inline float gelu_tanh(float x) {
-    const float t = x * fmaf(kGeluB, x * x, kGeluA);
-    float y = x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
-    if (t > 120.0f) y = gelu_far_negative(x, t);
-    return y;
+// GELU over N values in registers. The common path is branch-free; lanes
+// with t > kGeluFarT are patched under one wave-uniform branch (a ballot),
+// so the fast path never diverges. NaN stays NaN, +inf -> +inf,
+// -inf -> -0, +-0 -> +-0.
+template <int N>
+__device__ inline void gelu_tanh_n(float (&v)[N]) {
+    float t[N];
+    float tmax = -__builtin_inff();
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        t[j] = gelu_t(v[j]);
+        tmax = fmaxf(tmax, t[j]);
+    }
+    float y[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j) y[j] = v[j] * __builtin_amdgcn_rcpf(1.0f + exp2_raw(t[j]));
+    if (__builtin_amdgcn_ballot_w64(tmax > kGeluFarT) != 0) {
+#pragma unroll
+        for (int j = 0; j < N; ++j)
+            if (t[j] > kGeluFarT) y[j] = gelu_far(v[j], t[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < N; ++j) v[j] = y[j];
 }
 
 // ------------------------------------------------------- wave reductions --
@@ -171,8 +204,8 @@ __device__ inline float wave_sum(float v) {
 // factor 1.
 __device__ inline void ml_merge(float& m, float& l, float m2, float l2) {
     const float mn = fmaxf(m, m2);
-    const float f1 = (m == mn) ? 1.0f : __builtin_amdgcn_exp2f((m - mn) * kLog2e);
-    const float f2 = (m2 == mn) ? 1.0f : __builtin_amdgcn_exp2f((m2 - mn) * kLog2e);
+    const float f1 = (m == mn) ? 1.0f : exp2_raw((m - mn) * kLog2e);
+    const float f2 = (m2 == mn) ? 1.0f : exp2_raw((m2 - mn) * kLog2e);
     l = l * f1 + l2 * f2;
     m = mn;
 }

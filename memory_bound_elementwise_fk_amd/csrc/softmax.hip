@@ -1,234 +1,17 @@
-// softmax.hip -- row softmax kernels for gfx950.
-//
-// The operation, per row: m = max_j x_j; s = sum_j exp(x_j - m);
-// y_j = exp(x_j - m) / s ("CS336 lecture 6" notes, section 5.2: one block
-// per row, load the row on chip, max, exponentials and sum, normalise,
-// write back). exp(x - m) is evaluated as 2^((x - m) log2e) with the
-// hardware exp2; the max element gives exactly 2^0 = 1, so a one-column row
-// is exactly 1 and a constant row of 2^k columns exactly 2^-k.
-//
-// Single-pass kernel (rows up to the on-chip capacity): the row is held in
-// the VGPRs of the lanes that own it -- WPR waves per row, VPL 16-byte
-// vectors per lane -- so HBM is read once and written once. Reductions run
-// lane-local, then across the wave with DPP moves, then across the row's
-// waves through LDS, always in a fixed order (bitwise reproducible).
-//
-// Online kernel (any width, used above the capacity): one workgroup per row
-// streams the row in chunks keeping a per-lane running max m and running
-// sum l; when the max grows, l is rescaled by 2^((m_old - m_new) log2e)
-// ("Lecture 6: GPU Kernels and Triton", section 7.2 "Online Softmax", here
-// without the attention accumulator). Lane states merge by the same rule.
-// Pass 2 re-reads the row, last chunk first (the most recently read bytes
-// are the likeliest to still be in L2 / Infinity Cache), and writes
-// 2^((x - m) log2e) / l.
-#include "device_common.hpp"
+// softmax.hip -- launchers of the row softmax kernels in softmax_kernels.hpp:
+// the single-pass kernel for rows up to the on-chip capacity, the online
+// two-pass kernel above it.
+#include <atomic>
+
 #include "launch.hpp"
+#include "softmax_kernels.hpp"
 
 namespace fk {
 namespace {
 
-constexpr float kNegInf = -__builtin_inff();
 // grid * block stays below 2^31 work-items (the dispatch packet holds the
 // grid size in work-items as 32 bits); rows beyond it are grid-strided.
 constexpr int64_t kMaxWorkItems = int64_t(1) << 31;
-
-template <class IO>
-__device__ inline const char* row_ptr(const void* p, int64_t row, int64_t ld) {
-    return static_cast<const char*>(p) + row * ld * IO::kBytes;
-}
-template <class IO>
-__device__ inline char* row_ptr(void* p, int64_t row, int64_t ld) {
-    return static_cast<char*>(p) + row * ld * IO::kBytes;
-}
-
-// Load the E = VPL*V values a lane owns in one span of a row, starting at
-// column c0. VEC layout: vectors k*LANES + lane (16-byte loads); scalar
-// layout: columns k*LANES + lane. Columns >= cols read as -inf.
-template <class IO, int VPL, int LANES, bool VEC>
-__device__ inline void load_span(const char* xr, int64_t cols, int64_t c0, int lane,
-                                 float (&v)[VPL * IO::kVec]) {
-    constexpr int V = IO::kVec;
-    if constexpr (VEC) {
-#pragma unroll
-        for (int k = 0; k < VPL; ++k) {
-            const int64_t c = c0 + (int64_t(k) * LANES + lane) * V;
-            if (c + V <= cols) {
-                IO::unpack(ld16<false>(reinterpret_cast<const u32x4*>(xr + c * IO::kBytes)),
-                           &v[k * V]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < V; ++e)
-                    v[k * V + e] = (c + e < cols) ? IO::load1(xr, c + e) : kNegInf;
-            }
-        }
-    } else {
-#pragma unroll
-        for (int k = 0; k < VPL * V; ++k) {
-            const int64_t c = c0 + int64_t(k) * LANES + lane;
-            v[k] = c < cols ? IO::load1(xr, c) : kNegInf;
-        }
-    }
-}
-
-template <class IO, int VPL, int LANES, bool VEC>
-__device__ inline void store_span(char* yr, int64_t cols, int64_t c0, int lane,
-                                  const float (&v)[VPL * IO::kVec]) {
-    constexpr int V = IO::kVec;
-    if constexpr (VEC) {
-#pragma unroll
-        for (int k = 0; k < VPL; ++k) {
-            const int64_t c = c0 + (int64_t(k) * LANES + lane) * V;
-            if (c + V <= cols) {
-                st16<false>(reinterpret_cast<u32x4*>(yr + c * IO::kBytes), IO::pack(&v[k * V]));
-            } else {
-#pragma unroll
-                for (int e = 0; e < V; ++e)
-                    if (c + e < cols) IO::store1(yr, c + e, v[k * V + e]);
-            }
-        }
-    } else {
-#pragma unroll
-        for (int k = 0; k < VPL * V; ++k) {
-            const int64_t c = c0 + int64_t(k) * LANES + lane;
-            if (c < cols) IO::store1(yr, c, v[k]);
-        }
-    }
-}
-
-template <int WPR>
-constexpr int reg_threads() {
-    return WPR * kWave > 256 ? WPR * kWave : 256;
-}
-
-// ------------------------------------------------- single-pass kernel -----
-template <class IO, int WPR, int VPL, bool VEC>
-__global__ __launch_bounds__(reg_threads<WPR>()) void softmax_reg_kernel(
-    const void* x, void* y, int64_t rows, int64_t cols, int64_t ldx, int64_t ldy) {
-    constexpr int V = IO::kVec;
-    constexpr int E = VPL * V;
-    constexpr int kRowLanes = WPR * kWave;
-    constexpr int kRowsPerWg = reg_threads<WPR>() / kRowLanes;
-    __shared__ float red[kRowsPerWg * WPR];
-
-    const int sub = threadIdx.x / kRowLanes;  // which row of the WG
-    const int lr = threadIdx.x % kRowLanes;   // lane within the row's lanes
-    const int wave = lr / kWave;
-    const int lane = threadIdx.x % kWave;
-
-    // Every wave runs every iteration (the barriers are workgroup-wide);
-    // a row index past the end only masks its loads and stores.
-    for (int64_t rb = int64_t(blockIdx.x) * kRowsPerWg; rb < rows;
-         rb += int64_t(gridDim.x) * kRowsPerWg) {
-        const int64_t row = rb + sub;
-        const bool active = row < rows;
-        float v[E];
-        if (active) {
-            load_span<IO, VPL, kRowLanes, VEC>(row_ptr<IO>(x, row, ldx), cols, 0, lr, v);
-        } else {
-#pragma unroll
-            for (int i = 0; i < E; ++i) v[i] = kNegInf;
-        }
-
-        // row max
-        float m = kNegInf;
-#pragma unroll
-        for (int i = 0; i < E; ++i) m = fmaxf(m, v[i]);
-        m = wave_max(m);
-        if constexpr (WPR > 1) {
-            if (lane == 0) red[sub * WPR + wave] = m;
-            __syncthreads();
-            m = red[sub * WPR];
-#pragma unroll
-            for (int w = 1; w < WPR; ++w) m = fmaxf(m, red[sub * WPR + w]);
-            __syncthreads();
-        }
-
-        // exponentials and their sum (masked columns give 2^-inf = 0)
-        float s = 0.0f;
-#pragma unroll
-        for (int i = 0; i < E; ++i) {
-            const float e = exp2_full((v[i] - m) * kLog2e);
-            v[i] = e;
-            s += e;
-        }
-        s = wave_sum(s);
-        if constexpr (WPR > 1) {
-            if (lane == 0) red[sub * WPR + wave] = s;
-            __syncthreads();
-            s = red[sub * WPR];
-#pragma unroll
-            for (int w = 1; w < WPR; ++w) s += red[sub * WPR + w];
-            __syncthreads();
-        }
-
-        // normalise and write back
-        const float r = 1.0f / s;
-#pragma unroll
-        for (int i = 0; i < E; ++i) v[i] *= r;
-        if (active) store_span<IO, VPL, kRowLanes, VEC>(row_ptr<IO>(y, row, ldy), cols, 0, lr, v);
-    }
-}
-
-// ---------------------------------------------------------- online kernel -
-template <class IO, int THREADS, int VPL, bool VEC>
-__global__ __launch_bounds__(THREADS) void softmax_online_kernel(
-    const void* x, void* y, int64_t rows, int64_t cols, int64_t ldx, int64_t ldy) {
-    constexpr int E = VPL * IO::kVec;
-    constexpr int64_t kChunk = int64_t(THREADS) * E;
-    constexpr int kWaves = THREADS / kWave;
-    __shared__ float red_m[kWaves];
-    __shared__ float red_l[kWaves];
-
-    const int tid = threadIdx.x;
-    const int lane = tid % kWave;
-    const int wave = tid / kWave;
-    const int64_t nchunks = (cols + kChunk - 1) / kChunk;
-
-    for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
-        const char* xr = row_ptr<IO>(x, row, ldx);
-        char* yr = row_ptr<IO>(y, row, ldy);
-
-        // pass 1: running (m, l) per lane
-        float m = kNegInf, l = 0.0f;
-        for (int64_t c = 0; c < nchunks; ++c) {
-            float v[E];
-            load_span<IO, VPL, THREADS, VEC>(xr, cols, c * kChunk, tid, v);
-            float cm = kNegInf;
-#pragma unroll
-            for (int i = 0; i < E; ++i) cm = fmaxf(cm, v[i]);
-            const float mn = fmaxf(m, cm);
-            if (mn != kNegInf) {  // while every value seen is -inf, l stays 0
-                if (mn != m) l *= __builtin_amdgcn_exp2f((m - mn) * kLog2e);
-                m = mn;
-#pragma unroll
-                for (int i = 0; i < E; ++i) l += __builtin_amdgcn_exp2f((v[i] - m) * kLog2e);
-            }
-        }
-
-        // merge the lanes' states: wave (DPP), then the waves (LDS)
-        wave_ml(m, l);
-        if (lane == 0) {
-            red_m[wave] = m;
-            red_l[wave] = l;
-        }
-        __syncthreads();
-        m = red_m[0];
-        l = red_l[0];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w) ml_merge(m, l, red_m[w], red_l[w]);
-        __syncthreads();
-
-        // pass 2: normalise, last chunk first
-        const float r = 1.0f / l;
-        for (int64_t c = nchunks - 1; c >= 0; --c) {
-            float v[E];
-            load_span<IO, VPL, THREADS, VEC>(xr, cols, c * kChunk, tid, v);
-#pragma unroll
-            for (int i = 0; i < E; ++i) v[i] = exp2_full((v[i] - m) * kLog2e) * r;
-            store_span<IO, VPL, THREADS, VEC>(yr, cols, c * kChunk, tid, v);
-        }
-    }
-}
 
 // ----------------------------------------------------------------- launch -
 template <class... Args>
@@ -297,15 +80,61 @@ hipError_t launch_online(const void* x, void* y, int64_t rows, int64_t cols, int
                          ldx, ldy);
 }
 
+// Split shape: 256-lane blocks, 32 values per lane -> 8192-column slices.
+constexpr int kSplitThreads = 256;
+template <class IO>
+constexpr int kSplitVpl = 32 / IO::kVec;
+template <class IO>
+constexpr int64_t kSplitWidth = int64_t(kSplitThreads) * 32;
+
+std::atomic<int64_t> g_split_wait_limit{int64_t(1) << 20};
+
+template <class IO>
+int64_t split_parts(int64_t rows, int64_t cols) {
+    const int64_t parts = (cols + kSplitWidth<IO> - 1) / kSplitWidth<IO>;
+    if (cols <= reg_capacity<IO>(kRegShapes[kNumRegShapes - 1])) return 0;  // on-chip path
+    if (parts > kSplitMaxParts) return 0;
+    if (rows > (kMaxWorkItems / kSplitThreads) / parts) return 0;  // one block per slice
+    return parts;
+}
+
+int64_t split_ws_bytes(int64_t rows, int64_t parts) {
+    const int64_t depart = (rows * 4 + 7) / 8 * 8;
+    return rows * parts * 8 + depart;
+}
+
+template <class IO>
+hipError_t launch_split(const void* x, void* y, int64_t rows, int64_t cols, int64_t ldx,
+                        int64_t ldy, int64_t parts, void* ws, bool vec, hipStream_t s) {
+    constexpr int VPL = kSplitVpl<IO>;
+    const void* fn =
+        vec ? reinterpret_cast<const void*>(&softmax_split_kernel<IO, kSplitThreads, VPL, true>)
+            : reinterpret_cast<const void*>(&softmax_split_kernel<IO, kSplitThreads, VPL, false>);
+    auto* slots = static_cast<unsigned long long*>(ws);
+    auto* depart = reinterpret_cast<unsigned int*>(slots + rows * parts);
+    const int p = static_cast<int>(parts);
+    const int64_t spin = g_split_wait_limit.load(std::memory_order_relaxed);
+    return launch_kernel(fn, rows * parts, kSplitThreads, s, x, y, rows, cols, ldx, ldy, p, slots,
+                         depart, spin);
+}
+
+__global__ __launch_bounds__(256) void zero_fill_kernel(unsigned long long* p, int64_t n) {
+    const int64_t stride = int64_t(gridDim.x) * 256;
+    for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += stride) p[i] = 0ull;
+}
+
 template <class IO>
 hipError_t launch_softmax_t(const void* x, void* y, int64_t rows, int64_t cols, int64_t ldx,
-                            int64_t ldy, bool online, hipStream_t s) {
+                            int64_t ldy, bool online, void* ws, int64_t ws_bytes, hipStream_t s) {
     const bool vec = ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15u) == 0 &&
                      (ldx * IO::kBytes) % 16 == 0 && (ldy * IO::kBytes) % 16 == 0;
     if (!online) {
         for (int i = 0; i < kNumRegShapes; ++i)
             if (cols <= reg_capacity<IO>(kRegShapes[i]))
                 return dispatch_reg<IO>(i, x, y, rows, cols, ldx, ldy, vec, s);
+        const int64_t parts = split_parts<IO>(rows, cols);
+        if (parts > 0 && ws != nullptr && ws_bytes >= split_ws_bytes(rows, parts))
+            return launch_split<IO>(x, y, rows, cols, ldx, ldy, parts, ws, vec, s);
     }
     return launch_online<IO>(x, y, rows, cols, ldx, ldy, vec, s);
 }
@@ -317,10 +146,27 @@ int64_t softmax_onchip_max_cols(Dtype dt) {
                       : reg_capacity<IoBF16>(kRegShapes[kNumRegShapes - 1]);
 }
 
+int64_t softmax_workspace_bytes(int64_t rows, int64_t cols, Dtype dt) {
+    const int64_t parts = dt == kF32 ? split_parts<IoF32>(rows, cols) : split_parts<IoBF16>(rows, cols);
+    return parts > 0 ? split_ws_bytes(rows, parts) : 0;
+}
+
+int64_t split_wait_limit() { return g_split_wait_limit.load(); }
+
+int64_t set_split_wait_limit(int64_t polls) { return g_split_wait_limit.exchange(polls); }
+
+hipError_t launch_zero_fill(void* p, int64_t nbytes, hipStream_t s) {
+    const int64_t n = nbytes / 8;
+    const int64_t grid = n / 256 + 1 < 4096 ? n / 256 + 1 : 4096;
+    return launch_kernel(reinterpret_cast<const void*>(&zero_fill_kernel), grid, 256, s,
+                         static_cast<unsigned long long*>(p), n);
+}
+
 hipError_t launch_softmax(const void* x, void* y, int64_t rows, int64_t cols, int64_t ldx,
-                          int64_t ldy, Dtype dt, bool online, hipStream_t s) {
-    return dt == kF32 ? launch_softmax_t<IoF32>(x, y, rows, cols, ldx, ldy, online, s)
-                      : launch_softmax_t<IoBF16>(x, y, rows, cols, ldx, ldy, online, s);
+                          int64_t ldy, Dtype dt, bool online, void* ws, int64_t ws_bytes,
+                          hipStream_t s) {
+    return dt == kF32 ? launch_softmax_t<IoF32>(x, y, rows, cols, ldx, ldy, online, ws, ws_bytes, s)
+                      : launch_softmax_t<IoBF16>(x, y, rows, cols, ldx, ldy, online, ws, ws_bytes, s);
 }
 
 }  // namespace fk

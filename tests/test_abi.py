@@ -39,7 +39,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("fk_gelu_tanh", "fk_elementwise_chain", "fk_softmax_rows",
-                 "fk_softmax_rows_online", "fk_softmax_onchip_max_cols", "fk_copy",
+                 "fk_softmax_rows_online", "fk_softmax_rows_ws", "fk_softmax_workspace_bytes",
+                 "fk_set_split_wait_limit", "fk_softmax_onchip_max_cols", "fk_copy",
                  "fk_status_string"):
         assert want in names
 
@@ -117,6 +118,49 @@ def test_softmax_validation(L, name):
     assert s(A, A, 4, 10, 10, 12, 0, None) == fk.FK_ERR_OVERLAP
     assert s(A, A + 40, 4, 10, 20, 20, 0, None) == fk.FK_ERR_OVERLAP
     assert s(A, B, 2**40, 2**30, 2**30, 2**30, 0, None) == fk.FK_ERR_UNSUPPORTED
+
+
+def test_softmax_workspace_query(L):
+    q = L.fk_softmax_workspace_bytes
+    # rows that fit on chip need none
+    assert q(32768, 4096, fk.FK_BF16) == 0
+    assert q(4096, 32768, fk.FK_F32) == 0
+    assert q(10, 65536, fk.FK_BF16) == 0
+    assert q(0, 10**6, fk.FK_F32) == 0 and q(10, 0, fk.FK_F32) == 0
+    # rows * slices * 8 + rows * 4 rounded up to 8, slices = ceil(cols / 8192)
+    assert q(1024, 131072, fk.FK_F32) == 1024 * 16 * 8 + 4096
+    assert q(3, 32769, fk.FK_F32) == 3 * 5 * 8 + 16
+    assert q(7, 65537, fk.FK_BF16) == 7 * 9 * 8 + 32
+    assert q(1, 64 * 8192, fk.FK_F32) == 64 * 8 + 8
+    assert q(1, 64 * 8192 + 1, fk.FK_F32) == 0      # beyond 64 slices: online path
+    assert q(-1, 10, fk.FK_F32) == fk.FK_ERR_INVALID_ARG
+    assert q(1, 10, 9) == fk.FK_ERR_INVALID_ARG
+
+
+def test_softmax_ws_validation(L):
+    s = L.fk_softmax_rows_ws
+    rows, cols = 4, 40000                      # needs a workspace (fp32, 5 slices)
+    need = L.fk_softmax_workspace_bytes(rows, cols, fk.FK_F32)
+    W = 0x7F0000800000
+    assert need > 0
+    assert s(A, B, rows, cols, cols, cols, 0, None, 0, None) == fk.FK_ERR_INVALID_ARG
+    assert s(A, B, rows, cols, cols, cols, 0, W, need - 8, None) == fk.FK_ERR_INVALID_ARG
+    assert s(A, B, rows, cols, cols, cols, 0, W + 4, need, None) == fk.FK_ERR_INVALID_ARG
+    assert s(A, B, rows, cols, cols, cols, 0, W, -1, None) == fk.FK_ERR_INVALID_ARG
+    assert s(A, B, rows, cols, cols, cols, 0, A + 64, need, None) == fk.FK_ERR_OVERLAP
+    assert s(A, B, rows, cols, cols, cols, 0, B, need, None) == fk.FK_ERR_OVERLAP
+    assert s(A, B, 0, cols, cols, cols, 0, None, 0, None) == fk.FK_OK     # empty
+    assert s(A, B, rows, cols, cols - 1, cols, 0, W, need, None) == fk.FK_ERR_INVALID_ARG
+
+
+def test_split_wait_limit(L):
+    prev = L.fk_set_split_wait_limit(123)
+    try:
+        assert prev >= 0
+        assert L.fk_set_split_wait_limit(-1) == fk.FK_ERR_INVALID_ARG
+        assert L.fk_set_split_wait_limit(456) == 123
+    finally:
+        L.fk_set_split_wait_limit(prev)
 
 
 def test_copy_validation(L):

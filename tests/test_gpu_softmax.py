@@ -51,9 +51,12 @@ def test_c4_softmax_bf16_full_size():
     assert np.all(got[x == wl.BF16_MINUS_1E4] == 0)        # masked entries are exactly 0
 
 
-def test_c5a_softmax_fp32_full_size_online_path():
+def test_c5a_softmax_fp32_full_size_self_managed():
+    # wider than on-chip capacity: fk_softmax_rows takes the split path with
+    # a workspace it allocates itself
     x = wl.make_input("C5a")
-    assert x.shape[1] > fk.fk_softmax_onchip_max_cols(torch.float32)   # forces the online path
+    assert x.shape[1] > fk.fk_softmax_onchip_max_cols(torch.float32)
+    assert fk.fk_softmax_workspace_bytes(*x.shape, torch.float32) > 0
     xt = to_dev(x)
     y = torch.empty_like(xt)
     fk.fk_softmax_rows(xt, y)
