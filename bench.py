@@ -305,6 +305,23 @@ def measure_extras(fk, wl, torch, xs, ys, stream):
                                 fk.fk_elementwise_chain(t2, t3, ops[2:])))
     fb = wl.algorithmic_bytes("C3")
     ub = wl.algorithmic_bytes("C3", unfused=True)
+
+    # C3 without per-launch event overhead: 16 input/output pairs (1 GiB,
+    # four times the Infinity Cache) launched back to back between two events
+    pairs = [(torch.empty_like(x).copy_(x), torch.empty_like(x)) for _ in range(16)]
+    reps = 64
+
+    def rotating():
+        for k in range(reps):
+            a_, b_ = pairs[k % len(pairs)]
+            fk.fk_elementwise_chain(a_, b_, ops)
+
+    rot_ms = avg_ms(rotating, 1) / reps
+    out["chain_rotating_buffers"] = {
+        "ms": round(rot_ms, 5), "bytes": fb, "GBps": round(fb / (rot_ms * 1e-3) / 1e9, 1),
+        "frac_of_peak": round(fb / (rot_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "note": f"{reps} back-to-back launches over 16 rotating 32 MiB input/output pairs"}
+    del pairs
     out["chain_fused_vs_unfused"] = {
         "fused_ms": round(fused_ms, 5), "unfused_ms": round(unfused_ms, 5),
         "fused_bytes": fb, "unfused_bytes": ub,

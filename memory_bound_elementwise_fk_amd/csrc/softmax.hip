@@ -25,12 +25,19 @@ int64_t clamp_grid(int64_t g, int threads) {
     return g < 1 ? 1 : (g > cap ? cap : g);
 }
 
-// Single-pass shapes (waves per row, vectors per lane), smallest first.
+// Single-pass shapes (waves per row, 16-byte vectors per lane), smallest
+// first; the first that covers the row is used. At most 4 vectors per lane
+// until the widest shape: on MI355X a bf16 4096-column row ran 12 % faster
+// as 2 waves x 4 vectors than as 1 wave x 8 (fewer VGPRs, more waves in
+// flight).
 struct RegShape {
     int wpr, vpl;
 };
-constexpr RegShape kRegShapes[] = {{1, 1}, {1, 2}, {1, 4}, {1, 8},
-                                   {2, 8}, {4, 8}, {8, 8}, {16, 8}};
+constexpr RegShape kRegShapes[] = {{1, 1}, {1, 2}, {1, 4}, {2, 4},
+                                   {4, 4}, {8, 4}, {16, 4}, {16, 8}};
+// Row data is read once and written once: non-temporal loads and stores
+// (measured 4-9 % faster on the C4 and C5a shapes).
+constexpr bool kRowNT = true;
 constexpr int kNumRegShapes = sizeof(kRegShapes) / sizeof(kRegShapes[0]);
 
 template <class IO>
@@ -44,8 +51,9 @@ hipError_t launch_reg(const void* x, void* y, int64_t rows, int64_t cols, int64_
     constexpr int kThreads = reg_threads<WPR>();
     constexpr int kRowsPerWg = kThreads / (WPR * kWave);
     const int64_t grid = clamp_grid((rows + kRowsPerWg - 1) / kRowsPerWg, kThreads);
-    const void* fn = vec ? reinterpret_cast<const void*>(&softmax_reg_kernel<IO, WPR, VPL, true>)
-                         : reinterpret_cast<const void*>(&softmax_reg_kernel<IO, WPR, VPL, false>);
+    const void* fn =
+        vec ? reinterpret_cast<const void*>(&softmax_reg_kernel<IO, WPR, VPL, true, kRowNT>)
+            : reinterpret_cast<const void*>(&softmax_reg_kernel<IO, WPR, VPL, false>);
     return launch_kernel(fn, grid, kThreads, s, x, y, rows, cols, ldx, ldy);
 }
 
@@ -56,10 +64,10 @@ hipError_t dispatch_reg(int shape, const void* x, void* y, int64_t rows, int64_t
         case 0: return launch_reg<IO, 1, 1>(x, y, rows, cols, ldx, ldy, vec, s);
         case 1: return launch_reg<IO, 1, 2>(x, y, rows, cols, ldx, ldy, vec, s);
         case 2: return launch_reg<IO, 1, 4>(x, y, rows, cols, ldx, ldy, vec, s);
-        case 3: return launch_reg<IO, 1, 8>(x, y, rows, cols, ldx, ldy, vec, s);
-        case 4: return launch_reg<IO, 2, 8>(x, y, rows, cols, ldx, ldy, vec, s);
-        case 5: return launch_reg<IO, 4, 8>(x, y, rows, cols, ldx, ldy, vec, s);
-        case 6: return launch_reg<IO, 8, 8>(x, y, rows, cols, ldx, ldy, vec, s);
+        case 3: return launch_reg<IO, 2, 4>(x, y, rows, cols, ldx, ldy, vec, s);
+        case 4: return launch_reg<IO, 4, 4>(x, y, rows, cols, ldx, ldy, vec, s);
+        case 5: return launch_reg<IO, 8, 4>(x, y, rows, cols, ldx, ldy, vec, s);
+        case 6: return launch_reg<IO, 16, 4>(x, y, rows, cols, ldx, ldy, vec, s);
         default: return launch_reg<IO, 16, 8>(x, y, rows, cols, ldx, ldy, vec, s);
     }
 }
@@ -108,7 +116,7 @@ hipError_t launch_split(const void* x, void* y, int64_t rows, int64_t cols, int6
                         int64_t ldy, int64_t parts, void* ws, bool vec, hipStream_t s) {
     constexpr int VPL = kSplitVpl<IO>;
     const void* fn =
-        vec ? reinterpret_cast<const void*>(&softmax_split_kernel<IO, kSplitThreads, VPL, true>)
+        vec ? reinterpret_cast<const void*>(&softmax_split_kernel<IO, kSplitThreads, VPL, true, kRowNT>)
             : reinterpret_cast<const void*>(&softmax_split_kernel<IO, kSplitThreads, VPL, false>);
     auto* slots = static_cast<unsigned long long*>(ws);
     auto* depart = reinterpret_cast<unsigned int*>(slots + rows * parts);

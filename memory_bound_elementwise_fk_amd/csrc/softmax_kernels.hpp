@@ -44,7 +44,7 @@ __device__ inline char* row_ptr(void* p, int64_t row, int64_t ld) {
 // column c0. VEC layout: vectors k*LANES + lane (16-byte loads); scalar
 // layout: columns k*LANES + lane. Columns >= cols read as -inf. A span that
 // lies entirely inside the row (a uniform test) takes the unmasked path.
-template <class IO, int VPL, int LANES, bool VEC>
+template <class IO, int VPL, int LANES, bool VEC, bool NT = false>
 __device__ inline void load_span(const char* xr, int64_t cols, int64_t c0, int lane,
                                  float (&v)[VPL * IO::kVec]) {
     constexpr int V = IO::kVec;
@@ -54,7 +54,7 @@ __device__ inline void load_span(const char* xr, int64_t cols, int64_t c0, int l
             u32x4 w[VPL];
 #pragma unroll
             for (int k = 0; k < VPL; ++k)
-                w[k] = ld16<false>(reinterpret_cast<const u32x4*>(
+                w[k] = ld16<NT>(reinterpret_cast<const u32x4*>(
                     xr + (c0 + (int64_t(k) * LANES + lane) * V) * IO::kBytes));
 #pragma unroll
             for (int k = 0; k < VPL; ++k) IO::unpack(w[k], &v[k * V]);
@@ -64,7 +64,7 @@ __device__ inline void load_span(const char* xr, int64_t cols, int64_t c0, int l
         for (int k = 0; k < VPL; ++k) {
             const int64_t c = c0 + (int64_t(k) * LANES + lane) * V;
             if (c + V <= cols) {
-                IO::unpack(ld16<false>(reinterpret_cast<const u32x4*>(xr + c * IO::kBytes)),
+                IO::unpack(ld16<NT>(reinterpret_cast<const u32x4*>(xr + c * IO::kBytes)),
                            &v[k * V]);
             } else {
 #pragma unroll
@@ -81,7 +81,7 @@ __device__ inline void load_span(const char* xr, int64_t cols, int64_t c0, int l
     }
 }
 
-template <class IO, int VPL, int LANES, bool VEC>
+template <class IO, int VPL, int LANES, bool VEC, bool NT = false>
 __device__ inline void store_span(char* yr, int64_t cols, int64_t c0, int lane,
                                   const float (&v)[VPL * IO::kVec]) {
     constexpr int V = IO::kVec;
@@ -90,16 +90,16 @@ __device__ inline void store_span(char* yr, int64_t cols, int64_t c0, int lane,
         if (cols - c0 >= kSpan) {
 #pragma unroll
             for (int k = 0; k < VPL; ++k)
-                st16<false>(reinterpret_cast<u32x4*>(
-                                yr + (c0 + (int64_t(k) * LANES + lane) * V) * IO::kBytes),
-                            IO::pack(&v[k * V]));
+                st16<NT>(reinterpret_cast<u32x4*>(
+                             yr + (c0 + (int64_t(k) * LANES + lane) * V) * IO::kBytes),
+                         IO::pack(&v[k * V]));
             return;
         }
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
             const int64_t c = c0 + (int64_t(k) * LANES + lane) * V;
             if (c + V <= cols) {
-                st16<false>(reinterpret_cast<u32x4*>(yr + c * IO::kBytes), IO::pack(&v[k * V]));
+                st16<NT>(reinterpret_cast<u32x4*>(yr + c * IO::kBytes), IO::pack(&v[k * V]));
             } else {
 #pragma unroll
                 for (int e = 0; e < V; ++e)
@@ -123,7 +123,7 @@ constexpr int reg_threads() {
 }
 
 // ------------------------------------------------- single-pass kernel -----
-template <class IO, int WPR, int VPL, bool VEC>
+template <class IO, int WPR, int VPL, bool VEC, bool NT = false>
 __global__ __launch_bounds__(reg_threads<WPR>()) void softmax_reg_kernel(
     const void* x, void* y, int64_t rows, int64_t cols, int64_t ldx, int64_t ldy) {
     constexpr int V = IO::kVec;
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(reg_threads<WPR>()) void softmax_reg_kernel(
         const bool active = row < rows;
         float v[E];
         if (active) {
-            load_span<IO, VPL, kRowLanes, VEC>(row_ptr<IO>(x, row, ldx), cols, 0, lr, v);
+            load_span<IO, VPL, kRowLanes, VEC, NT>(row_ptr<IO>(x, row, ldx), cols, 0, lr, v);
         } else {
 #pragma unroll
             for (int i = 0; i < E; ++i) v[i] = kNegInf;
@@ -186,7 +186,8 @@ __global__ __launch_bounds__(reg_threads<WPR>()) void softmax_reg_kernel(
         const float r = 1.0f / s;
 #pragma unroll
         for (int i = 0; i < E; ++i) v[i] *= r;
-        if (active) store_span<IO, VPL, kRowLanes, VEC>(row_ptr<IO>(y, row, ldy), cols, 0, lr, v);
+        if (active)
+            store_span<IO, VPL, kRowLanes, VEC, NT>(row_ptr<IO>(y, row, ldy), cols, 0, lr, v);
     }
 }
 
@@ -352,7 +353,7 @@ __device__ inline void row_stats_streamed(const char* xr, int64_t cols, float* r
     __syncthreads();
 }
 
-template <class IO, int THREADS, int VPL, bool VEC>
+template <class IO, int THREADS, int VPL, bool VEC, bool NT = false>
 __global__ __launch_bounds__(THREADS) void softmax_split_kernel(
     const void* x, void* y, int64_t rows, int64_t cols, int64_t ldx, int64_t ldy, int parts,
     unsigned long long* slots, unsigned int* depart, int64_t spin_limit) {
@@ -375,7 +376,7 @@ __global__ __launch_bounds__(THREADS) void softmax_split_kernel(
         const int64_t c0 = int64_t(p) * kW;
 
         float v[E];
-        load_span<IO, VPL, THREADS, VEC>(xr, cols, c0, tid, v);
+        load_span<IO, VPL, THREADS, VEC, NT>(xr, cols, c0, tid, v);
 
         // this slice's partial (m_p, l_p)
         float m = kNegInf;
@@ -427,7 +428,7 @@ __global__ __launch_bounds__(THREADS) void softmax_split_kernel(
         const float r = 1.0f / (L * kSoftmaxScale);
 #pragma unroll
         for (int i = 0; i < E; ++i) v[i] = softmax_numerator(v[i], M) * r;
-        store_span<IO, VPL, THREADS, VEC>(row_ptr<IO>(y, row, ldy), cols, c0, tid, v);
+        store_span<IO, VPL, THREADS, VEC, NT>(row_ptr<IO>(y, row, ldy), cols, c0, tid, v);
 
         // the last slice done with the row's slots clears them
         if (tid == 0) {
