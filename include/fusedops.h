@@ -163,6 +163,30 @@ int fk_softmax_rows_online(const void* x, void* y, int64_t rows, int64_t cols,
                            int64_t ldx, int64_t ldy, int dtype, void* stream);
 
 /*
+ * Fused LayerNorm over each row, optionally followed by tanh-GELU: with
+ * x_r, y_r as for fk_softmax_rows, mu = mean_j x_r[j],
+ * var = mean_j (x_r[j] - mu)^2 (biased),
+ * t_j = (x_r[j] - mu) / sqrt(var + eps) * gamma[j] + beta[j],
+ * y_r[j] = fuse_gelu ? GELU(t_j) : t_j. LayerNorm is the first stage of the
+ * LayerNorm -> Linear -> GELU fusion example of "Lecture 6: GPU Kernels and
+ * Triton", section 6.1 (the page gives no formula; this is the standard
+ * definition). One read of x and one write of y per element, fp32
+ * statistics (corrected two-pass over the row held in registers).
+ * gamma, beta: DEVICE arrays of cols elements of dtype, or NULL (1 and 0);
+ * they must not overlap y (FK_ERR_OVERLAP). eps: finite, >= 0.
+ * fuse_gelu: 0 or 1. Rows wider than fk_layernorm_max_cols(dtype) are
+ * FK_ERR_UNSUPPORTED. In place (y == x, same stride) is allowed.
+ */
+int fk_layernorm_rows(const void* x, void* y, int64_t rows, int64_t cols,
+                      int64_t ldx, int64_t ldy, const void* gamma,
+                      const void* beta, float eps, int fuse_gelu, int dtype,
+                      void* stream);
+
+/* Widest row fk_layernorm_rows accepts for dtype (32768 fp32, 65536 bf16),
+ * or FK_ERR_INVALID_ARG for an unknown dtype. Pure host query. */
+int64_t fk_layernorm_max_cols(int dtype);
+
+/*
  * Widest row (in columns) that fk_softmax_rows holds on chip for dtype, or
  * FK_ERR_INVALID_ARG for an unknown dtype. Pure host query.
  */

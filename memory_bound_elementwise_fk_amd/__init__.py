@@ -31,7 +31,8 @@ FK_MAX_OPS = 8
 __all__ = [
     "FusedOpsError", "lib", "fk_gelu_tanh", "fk_elementwise_chain", "fk_softmax_rows",
     "fk_softmax_rows_online", "fk_softmax_rows_ws", "fk_softmax_workspace_bytes",
-    "fk_set_split_wait_limit", "fk_softmax_onchip_max_cols", "fk_copy", "fk_status_string",
+    "fk_set_split_wait_limit", "fk_softmax_onchip_max_cols", "fk_layernorm_rows",
+    "fk_layernorm_max_cols", "fk_copy", "fk_status_string", "layernorm_rows",
     "gelu_tanh", "elementwise_chain", "softmax_rows",
 ]
 
@@ -75,6 +76,11 @@ def lib() -> ctypes.CDLL:
     L.fk_softmax_workspace_bytes.restype = i64
     L.fk_set_split_wait_limit.argtypes = [i64]
     L.fk_set_split_wait_limit.restype = i64
+    L.fk_layernorm_rows.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp, ctypes.c_float, i32, i32,
+                                    vp]
+    L.fk_layernorm_rows.restype = i32
+    L.fk_layernorm_max_cols.argtypes = [i32]
+    L.fk_layernorm_max_cols.restype = i64
     L.fk_softmax_onchip_max_cols.argtypes = [i32]
     L.fk_softmax_onchip_max_cols.restype = i64
     L.fk_copy.argtypes = [vp, vp, i64, vp]
@@ -244,6 +250,38 @@ def fk_softmax_onchip_max_cols(dtype) -> int:
     return int(v)
 
 
+def _param(p, x, name: str):
+    """Device pointer of an optional per-column parameter (None -> NULL)."""
+    if p is None:
+        return None
+    _device_tensor(p, name)
+    if p.dtype != x.dtype or p.dim() != 1 or p.numel() != x.shape[-1] or not p.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous 1-D tensor of x's dtype with one entry "
+                         f"per column")
+    if p.device != x.device:
+        raise ValueError(f"{name} is on another device than x")
+    return p.data_ptr()
+
+
+def fk_layernorm_rows(x, y, gamma=None, beta=None, eps: float = 1e-5, gelu: bool = False,
+                      stream=None) -> None:
+    """LayerNorm along each row of a 2-D x into y (optionally then tanh-GELU)."""
+    rows, cols, ldx, ldy, dt = _rows_pair(x, y, "fk_layernorm_rows")
+    g, b = _param(gamma, x, "gamma"), _param(beta, x, "beta")
+    with _torch().cuda.device(x.device):
+        _check(lib().fk_layernorm_rows(x.data_ptr(), y.data_ptr(), rows, cols, ldx, ldy, g, b,
+                                       float(eps), int(bool(gelu)), dt, _stream_handle(x, stream)),
+               "fk_layernorm_rows")
+
+
+def fk_layernorm_max_cols(dtype) -> int:
+    """Widest row fk_layernorm_rows accepts for a torch dtype or an FK_* code."""
+    v = lib().fk_layernorm_max_cols(_dtype_arg(dtype))
+    if v < 0:
+        raise FusedOpsError(int(v), "fk_layernorm_max_cols")
+    return int(v)
+
+
 def fk_copy(x, y, nbytes: int | None = None, stream=None) -> None:
     """Copy nbytes (default: all of x) from x to y on the device."""
     _device_tensor(x, "x")
@@ -273,4 +311,10 @@ def elementwise_chain(x, ops, stream=None):
 def softmax_rows(x, stream=None):
     y = _torch().empty(x.shape, dtype=x.dtype, device=x.device)
     fk_softmax_rows(x, y, stream)
+    return y
+
+
+def layernorm_rows(x, gamma=None, beta=None, eps: float = 1e-5, gelu: bool = False, stream=None):
+    y = _torch().empty(x.shape, dtype=x.dtype, device=x.device)
+    fk_layernorm_rows(x, y, gamma, beta, eps, gelu, stream)
     return y

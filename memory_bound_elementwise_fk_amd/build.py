@@ -18,8 +18,9 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 INCLUDE = ROOT / "include"
 LIB = PKG / "libfusedops.so"
-SOURCES = ["api.hip", "elementwise.hip", "softmax.hip"]
-HEADERS = ["device_common.hpp", "ew_kernels.hpp", "softmax_kernels.hpp", "launch.hpp"]
+SOURCES = ["api.hip", "elementwise.hip", "softmax.hip", "layernorm.hip"]
+HEADERS = ["device_common.hpp", "ew_kernels.hpp", "softmax_kernels.hpp", "layernorm_kernels.hpp",
+           "launch.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -178,6 +178,32 @@ int fk_softmax_rows_online(const void* x, void* y, int64_t rows, int64_t cols, i
     return softmax_launch(x, y, rows, cols, ldx, ldy, dtype, true, nullptr, 0, stream);
 }
 
+int fk_layernorm_rows(const void* x, void* y, int64_t rows, int64_t cols, int64_t ldx,
+                      int64_t ldy, const void* gamma, const void* beta, float eps, int fuse_gelu,
+                      int dtype, void* stream) {
+    bool skip = false;
+    const int st = check_rows(x, y, rows, cols, ldx, ldy, dtype, &skip);
+    if (st != FK_OK) return st;
+    if (!(eps >= 0.0f) || eps == std::numeric_limits<float>::infinity()) return FK_ERR_INVALID_ARG;
+    if (fuse_gelu != 0 && fuse_gelu != 1) return FK_ERR_INVALID_ARG;
+    if (skip) return FK_OK;
+    if (cols > fk::layernorm_max_cols(static_cast<fk::Dtype>(dtype))) return FK_ERR_UNSUPPORTED;
+    const int64_t es = esize(dtype);
+    const int64_t by = ((rows - 1) * ldy + cols) * es;
+    // gamma and beta are read by every row while y is written
+    if ((gamma != nullptr && ranges_overlap(gamma, cols * es, y, by)) ||
+        (beta != nullptr && ranges_overlap(beta, cols * es, y, by)))
+        return FK_ERR_OVERLAP;
+    return hip_status(fk::launch_layernorm(x, y, rows, cols, ldx, ldy, gamma, beta, eps, fuse_gelu,
+                                           static_cast<fk::Dtype>(dtype),
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int64_t fk_layernorm_max_cols(int dtype) {
+    if (!dtype_ok(dtype)) return FK_ERR_INVALID_ARG;
+    return fk::layernorm_max_cols(static_cast<fk::Dtype>(dtype));
+}
+
 int64_t fk_softmax_onchip_max_cols(int dtype) {
     if (!dtype_ok(dtype)) return FK_ERR_INVALID_ARG;
     return fk::softmax_onchip_max_cols(static_cast<fk::Dtype>(dtype));

@@ -89,19 +89,25 @@ __device__ inline void ew_ragged_tile(const u32x4* x, u32x4* y, int64_t n, int64
 }
 
 // x, y 16-byte aligned. Tile t covers vectors [t*T*U, (t+1)*T*U); lane l of
-// the workgroup owns vectors t*T*U + u*T + l, u < U. Tiles beyond the grid
-// are grid-strided (only for sizes past 2^31 work-items). x == y (in place)
-// is safe despite __restrict__: every address is loaded and stored by the
-// same lane, and the store depends on the loaded value.
-template <class IO, int T, int U, bool NT, class Op>
+// the workgroup owns vectors t*T*U + u*T + l, u < U. The host passes nfull,
+// the number of tiles without a ragged end (one tile more holds the ragged
+// end when n is not a multiple of the tile). With STRIDED false there is
+// exactly one workgroup per tile and no loop: with one 16-byte vector per
+// lane a workgroup lives for a single load and store, so per-workgroup
+// setup matters. STRIDED true loops over tiles (only for sizes past 2^31
+// work-items). x == y (in place) is safe despite __restrict__: every
+// address is loaded and stored by the same lane, and the store depends on
+// the loaded value.
+template <class IO, int T, int U, bool NT, bool STRIDED, class Op>
 __global__ __launch_bounds__(T) void ew_vec_kernel(const u32x4* __restrict__ x,
-                                                   u32x4* __restrict__ y, int64_t n, Op op) {
-    constexpr int V = IO::kVec;
+                                                   u32x4* __restrict__ y, int64_t n,
+                                                   int64_t nfull, Op op) {
     constexpr int64_t kTileVec = int64_t(T) * U;
-    const int64_t nvec = n / V;
-    const int64_t nfull = nvec / kTileVec;
-    const int64_t ntiles = (n + kTileVec * V - 1) / (kTileVec * V);
-    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const int64_t ntiles = STRIDED ? (n + kTileVec * IO::kVec - 1) / (kTileVec * IO::kVec) : 0;
+    for (int64_t tile = blockIdx.x;; tile += gridDim.x) {
+        if constexpr (STRIDED) {
+            if (tile >= ntiles) break;
+        }
         const int64_t v0 = tile * kTileVec + threadIdx.x;
         if (tile < nfull) {
             u32x4 w[U];
@@ -111,8 +117,9 @@ __global__ __launch_bounds__(T) void ew_vec_kernel(const u32x4* __restrict__ x,
 #pragma unroll
             for (int u = 0; u < U; ++u) st16<NT>(y + v0 + u * T, w[u]);
         } else {
-            ew_ragged_tile<IO, T, U, NT>(x, y, n, nvec, v0, op);
+            ew_ragged_tile<IO, T, U, NT>(x, y, n, n / IO::kVec, v0, op);
         }
+        if constexpr (!STRIDED) break;
     }
 }
 

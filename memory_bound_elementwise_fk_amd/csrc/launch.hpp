@@ -42,4 +42,11 @@ int64_t set_split_wait_limit(int64_t polls);
 // Fill nbytes (a multiple of 8, 8-byte aligned) with zeros on stream s.
 hipError_t launch_zero_fill(void* p, int64_t nbytes, hipStream_t s);
 
+// Fused LayerNorm (+ optional tanh-GELU) over rows of at most
+// layernorm_max_cols(dt) columns; gamma / beta may be null.
+hipError_t launch_layernorm(const void* x, void* y, int64_t rows, int64_t cols, int64_t ldx,
+                            int64_t ldy, const void* gamma, const void* beta, float eps, int gelu,
+                            Dtype dt, hipStream_t s);
+int64_t layernorm_max_cols(Dtype dt);
+
 }  // namespace fk

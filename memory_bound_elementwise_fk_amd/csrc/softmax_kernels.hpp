@@ -42,11 +42,12 @@ __device__ inline char* row_ptr(void* p, int64_t row, int64_t ld) {
 
 // Load the E = VPL*V values a lane owns in one span of a row, starting at
 // column c0. VEC layout: vectors k*LANES + lane (16-byte loads); scalar
-// layout: columns k*LANES + lane. Columns >= cols read as -inf. A span that
-// lies entirely inside the row (a uniform test) takes the unmasked path.
+// layout: columns k*LANES + lane. Columns >= cols read as `fill` (-inf for
+// the max/exp reductions, 0 for sums). A span that lies entirely inside the
+// row (a uniform test) takes the unmasked path.
 template <class IO, int VPL, int LANES, bool VEC, bool NT = false>
 __device__ inline void load_span(const char* xr, int64_t cols, int64_t c0, int lane,
-                                 float (&v)[VPL * IO::kVec]) {
+                                 float (&v)[VPL * IO::kVec], float fill = -__builtin_inff()) {
     constexpr int V = IO::kVec;
     constexpr int64_t kSpan = int64_t(VPL) * LANES * V;
     if constexpr (VEC) {
@@ -69,16 +70,25 @@ __device__ inline void load_span(const char* xr, int64_t cols, int64_t c0, int l
             } else {
 #pragma unroll
                 for (int e = 0; e < V; ++e)
-                    v[k * V + e] = (c + e < cols) ? IO::load1(xr, c + e) : kNegInf;
+                    v[k * V + e] = (c + e < cols) ? IO::load1(xr, c + e) : fill;
             }
         }
     } else {
 #pragma unroll
         for (int k = 0; k < VPL * V; ++k) {
             const int64_t c = c0 + int64_t(k) * LANES + lane;
-            v[k] = c < cols ? IO::load1(xr, c) : kNegInf;
+            v[k] = c < cols ? IO::load1(xr, c) : fill;
         }
     }
+}
+
+// Column (relative to the span start) of value i of a lane in load_span's
+// layout.
+template <class IO, int LANES, bool VEC>
+__device__ inline int64_t span_col(int i, int lane) {
+    constexpr int V = IO::kVec;
+    if constexpr (VEC) return (int64_t(i / V) * LANES + lane) * V + i % V;
+    else return int64_t(i) * LANES + lane;
 }
 
 template <class IO, int VPL, int LANES, bool VEC, bool NT = false>

@@ -51,6 +51,12 @@ def _load():
         "oracle_softmax_rows_f64": ([vp, vp, i64, i64, i64, i64], i32),
         "oracle_softmax_rows_f32": ([vp, vp, i64, i64, i64, i64, i32], i32),
         "oracle_softmax_rows_bf16": ([vp, vp, i64, i64, i64, i64, i32], i32),
+        "oracle_layernorm_rows_f64": ([vp, vp, i64, i64, i64, i64, vp, vp, ctypes.c_double, i32],
+                                      i32),
+        "oracle_layernorm_rows_f32": ([vp, vp, i64, i64, i64, i64, vp, vp, ctypes.c_double, i32,
+                                       i32], i32),
+        "oracle_layernorm_rows_bf16": ([vp, vp, i64, i64, i64, i64, vp, vp, ctypes.c_double, i32,
+                                        i32], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -178,4 +184,42 @@ def softmax_rows(x: np.ndarray, threads: int = 1, out: np.ndarray | None = None)
         raise TypeError(f"unsupported dtype {x.dtype}")
     if rc != 0:
         raise ValueError("invalid softmax sizes")
+    return out
+
+
+# ------------------------------------------------------------- layernorm --
+def layernorm_rows(x: np.ndarray, gamma: np.ndarray | None = None, beta: np.ndarray | None = None,
+                   eps: float = 1e-5, gelu: bool = False, threads: int = 1) -> np.ndarray:
+    """LayerNorm along the last axis of a 2-D array (float64, float32 or bf16 uint16).
+
+    y = (x - mean) / sqrt(var + eps) * gamma + beta (biased variance), then
+    tanh-GELU if ``gelu``; gamma and beta are per-column arrays of x's dtype
+    or None. Computed in double, rounded once to the storage type.
+    """
+    if x.ndim != 2:
+        raise ValueError("layernorm_rows expects a 2-D array")
+    rows, cols = x.shape
+    x = np.ascontiguousarray(x)
+    out = np.empty((rows, cols), x.dtype)
+    g = None if gamma is None else np.ascontiguousarray(gamma, x.dtype).ravel()
+    b = None if beta is None else np.ascontiguousarray(beta, x.dtype).ravel()
+    for a in (g, b):
+        if a is not None and a.size != cols:
+            raise ValueError("gamma and beta need one entry per column")
+    gp = None if g is None else _ptr(g)
+    bp = None if b is None else _ptr(b)
+    lib = _load()
+    if x.dtype == np.float64:
+        rc = lib.oracle_layernorm_rows_f64(_ptr(x), _ptr(out), rows, cols, cols, cols, gp, bp,
+                                           float(eps), int(gelu))
+    elif x.dtype == np.float32:
+        rc = lib.oracle_layernorm_rows_f32(_ptr(x), _ptr(out), rows, cols, cols, cols, gp, bp,
+                                           float(eps), int(gelu), threads)
+    elif x.dtype == np.uint16:
+        rc = lib.oracle_layernorm_rows_bf16(_ptr(x), _ptr(out), rows, cols, cols, cols, gp, bp,
+                                            float(eps), int(gelu), threads)
+    else:
+        raise TypeError(f"unsupported dtype {x.dtype}")
+    if rc != 0:
+        raise ValueError("invalid layernorm sizes or eps")
     return out

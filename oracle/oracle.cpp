@@ -24,6 +24,11 @@
 //  * Chain: "Lecture 6: GPU Kernels and Triton", section 1.1 (three
 //    consecutive elementwise ops) -- each op is applied in order and each
 //    intermediate is materialised in the I/O compute type (fp32).
+//  * LayerNorm: "Lecture 6: GPU Kernels and Triton", section 6.1 names it as
+//    the first kernel of the LayerNorm -> Linear -> GELU example without a
+//    formula; the standard definition over the last axis is used: mean, the
+//    biased variance, (x - mean) / sqrt(var + eps), then gamma and beta per
+//    column, optionally followed by the tanh-GELU above.
 //
 // Readings where the pages are silent (each also listed in the design notes):
 //  * GELU(-inf) = -0 (the limit), GELU(NaN) = NaN, GELU(+inf) = +inf.
@@ -123,6 +128,27 @@ void softmax_row(const double* x, double* y, int64_t cols) {
     for (int64_t j = 0; j < cols; ++j) y[j] = std::exp(x[j] - m) / s;
 }
 
+// ---------------------------------------------------------------- layernorm
+// One row in double: mu = sum_j x_j / n; var = sum_j (x_j - mu)^2 / n;
+// y_j = (x_j - mu) / sqrt(var + eps) * gamma_j + beta_j (gamma = 1, beta = 0
+// when absent), then y_j = GELU(y_j) if requested.
+void layernorm_row(const double* x, double* y, int64_t cols, const double* gamma,
+                   const double* beta, double eps, bool gelu) {
+    double sum = 0.0;
+    for (int64_t j = 0; j < cols; ++j) sum += x[j];
+    const double mu = sum / static_cast<double>(cols);
+    double sq = 0.0;
+    for (int64_t j = 0; j < cols; ++j) sq += (x[j] - mu) * (x[j] - mu);
+    const double var = sq / static_cast<double>(cols);
+    const double denom = std::sqrt(var + eps);
+    for (int64_t j = 0; j < cols; ++j) {
+        double v = (x[j] - mu) / denom;
+        if (gamma != nullptr) v *= gamma[j];
+        if (beta != nullptr) v += beta[j];
+        y[j] = gelu ? gelu_real(v) : v;
+    }
+}
+
 // ---------------------------------------------------------------- threads -
 // Run body(begin, end) over [0, n) split into contiguous pieces.
 template <class Body>
@@ -150,6 +176,31 @@ void softmax_rows_generic(const In* x, Out* y, int64_t rows, int64_t cols, int64
         for (int64_t r = r0; r < r1; ++r) {
             for (int64_t j = 0; j < cols; ++j) xin[j] = load(x[r * ldx + j]);
             softmax_row(xin.data(), yout.data(), cols);
+            for (int64_t j = 0; j < cols; ++j) y[r * ldy + j] = store(yout[j]);
+        }
+    });
+}
+
+template <class In, class Out, class Load, class Store>
+void layernorm_rows_generic(const In* x, Out* y, int64_t rows, int64_t cols, int64_t ldx,
+                            int64_t ldy, const In* gamma, const In* beta, double eps, bool gelu,
+                            int nthreads, Load load, Store store) {
+    std::vector<double> g, b;
+    if (gamma != nullptr) {
+        g.resize(static_cast<size_t>(cols));
+        for (int64_t j = 0; j < cols; ++j) g[j] = load(gamma[j]);
+    }
+    if (beta != nullptr) {
+        b.resize(static_cast<size_t>(cols));
+        for (int64_t j = 0; j < cols; ++j) b[j] = load(beta[j]);
+    }
+    const double* gp = gamma != nullptr ? g.data() : nullptr;
+    const double* bp = beta != nullptr ? b.data() : nullptr;
+    parallel_range(rows, nthreads, [&](int64_t r0, int64_t r1) {
+        std::vector<double> xin(static_cast<size_t>(cols)), yout(static_cast<size_t>(cols));
+        for (int64_t r = r0; r < r1; ++r) {
+            for (int64_t j = 0; j < cols; ++j) xin[j] = load(x[r * ldx + j]);
+            layernorm_row(xin.data(), yout.data(), cols, gp, bp, eps, gelu);
             for (int64_t j = 0; j < cols; ++j) y[r * ldy + j] = store(yout[j]);
         }
     });
@@ -239,6 +290,35 @@ int oracle_softmax_rows_bf16(const uint16_t* x, uint16_t* y, int64_t rows, int64
     softmax_rows_generic(x, y, rows, cols, ldx, ldy, nthreads,
                          [](uint16_t v) { return static_cast<double>(bf16_to_f32(v)); },
                          [](double v) { return f32_to_bf16(static_cast<float>(v)); });
+    return 0;
+}
+
+// ---- layernorm (returns 0, or -1 for invalid sizes) ----
+// gamma, beta: per-column arrays in the storage type of x, or NULL.
+int oracle_layernorm_rows_f64(const double* x, double* y, int64_t rows, int64_t cols,
+                              int64_t ldx, int64_t ldy, const double* gamma, const double* beta,
+                              double eps, int gelu) {
+    if (!softmax_args_ok(x, y, rows, cols, ldx, ldy) || !(eps >= 0.0)) return -1;
+    layernorm_rows_generic(x, y, rows, cols, ldx, ldy, gamma, beta, eps, gelu != 0, 1,
+                           [](double v) { return v; }, [](double v) { return v; });
+    return 0;
+}
+int oracle_layernorm_rows_f32(const float* x, float* y, int64_t rows, int64_t cols, int64_t ldx,
+                              int64_t ldy, const float* gamma, const float* beta, double eps,
+                              int gelu, int nthreads) {
+    if (!softmax_args_ok(x, y, rows, cols, ldx, ldy) || !(eps >= 0.0)) return -1;
+    layernorm_rows_generic(x, y, rows, cols, ldx, ldy, gamma, beta, eps, gelu != 0, nthreads,
+                           [](float v) { return static_cast<double>(v); },
+                           [](double v) { return static_cast<float>(v); });
+    return 0;
+}
+int oracle_layernorm_rows_bf16(const uint16_t* x, uint16_t* y, int64_t rows, int64_t cols,
+                               int64_t ldx, int64_t ldy, const uint16_t* gamma,
+                               const uint16_t* beta, double eps, int gelu, int nthreads) {
+    if (!softmax_args_ok(x, y, rows, cols, ldx, ldy) || !(eps >= 0.0)) return -1;
+    layernorm_rows_generic(x, y, rows, cols, ldx, ldy, gamma, beta, eps, gelu != 0, nthreads,
+                           [](uint16_t v) { return static_cast<double>(bf16_to_f32(v)); },
+                           [](double v) { return f32_to_bf16(static_cast<float>(v)); });
     return 0;
 }
 

@@ -41,7 +41,7 @@ def test_header_declares_the_entry_points():
     for want in ("fk_gelu_tanh", "fk_elementwise_chain", "fk_softmax_rows",
                  "fk_softmax_rows_online", "fk_softmax_rows_ws", "fk_softmax_workspace_bytes",
                  "fk_set_split_wait_limit", "fk_softmax_onchip_max_cols", "fk_copy",
-                 "fk_status_string"):
+                 "fk_status_string", "fk_layernorm_rows", "fk_layernorm_max_cols"):
         assert want in names
 
 
@@ -161,6 +161,27 @@ def test_split_wait_limit(L):
         assert L.fk_set_split_wait_limit(456) == 123
     finally:
         L.fk_set_split_wait_limit(prev)
+
+
+def test_layernorm_validation(L):
+    ln = L.fk_layernorm_rows
+    G = 0x7F0000900000
+    assert L.fk_layernorm_max_cols(fk.FK_F32) == 32768
+    assert L.fk_layernorm_max_cols(fk.FK_BF16) == 65536
+    assert L.fk_layernorm_max_cols(5) == fk.FK_ERR_INVALID_ARG
+    assert ln(A, B, 0, 10, 10, 10, None, None, 1e-5, 0, 0, None) == fk.FK_OK
+    assert ln(A, B, 4, 10, 10, 10, None, None, -1.0, 0, 0, None) == fk.FK_ERR_INVALID_ARG
+    assert ln(A, B, 4, 10, 10, 10, None, None, float("nan"), 0, 0, None) == fk.FK_ERR_INVALID_ARG
+    assert ln(A, B, 4, 10, 10, 10, None, None, float("inf"), 0, 0, None) == fk.FK_ERR_INVALID_ARG
+    assert ln(A, B, 4, 10, 10, 10, None, None, 1e-5, 2, 0, None) == fk.FK_ERR_INVALID_ARG
+    assert ln(A, B, 4, 10, 10, 10, None, None, 1e-5, 0, 7, None) == fk.FK_ERR_INVALID_ARG
+    assert ln(A, B, 4, 10, 9, 10, None, None, 1e-5, 0, 0, None) == fk.FK_ERR_INVALID_ARG
+    assert ln(A, B, 2, 32769, 32769, 32769, None, None, 1e-5, 0, 0, None) == fk.FK_ERR_UNSUPPORTED
+    assert ln(A, B, 2, 65537, 65537, 65537, None, None, 1e-5, 0, 1, None) == fk.FK_ERR_UNSUPPORTED
+    # gamma / beta must not overlap the output
+    assert ln(A, B, 4, 10, 10, 10, B + 8, None, 1e-5, 0, 0, None) == fk.FK_ERR_OVERLAP
+    assert ln(A, B, 4, 10, 10, 10, G, B + 100, 1e-5, 0, 0, None) == fk.FK_ERR_OVERLAP
+    assert ln(A, A + 8, 4, 10, 10, 10, None, None, 1e-5, 0, 0, None) == fk.FK_ERR_OVERLAP
 
 
 def test_copy_validation(L):
