@@ -322,6 +322,34 @@ def measure_extras(fk, wl, torch, xs, ys, stream):
         "frac_of_peak": round(fb / (rot_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "note": f"{reps} back-to-back launches over 16 rotating 32 MiB input/output pairs"}
     del pairs
+
+    # LayerNorm (+ GELU epilogue) on the C4 row shape (bf16 32768 x 4096) and
+    # the C2 row shape (fp32 4096 x 1000, rows shifted every 16th); the
+    # algorithmic bytes are one read of x and one write of y (gamma and beta,
+    # 2 * cols elements, are counted once)
+    from memory_bound_elementwise_fk_amd import workloads as wl_
+
+    ln = {}
+    xb = xs["C4"]
+    gb = torch.ones(xb.shape[1], dtype=xb.dtype, device=xb.device)
+    bb = torch.zeros_like(gb)
+    yb = torch.empty_like(xb)
+    ms = avg_ms(lambda: fk.fk_layernorm_rows(xb, yb, gb, bb, gelu=True), 20)
+    nb = 2 * xb.numel() * 2 + 2 * xb.shape[1] * 2
+    ln["bf16_32768x4096_gelu"] = {"ms": round(ms, 5), "bytes": nb,
+                                  "GBps": round(nb / (ms * 1e-3) / 1e9, 1),
+                                  "frac_of_peak": round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del yb
+    xf = wl_.to_torch(wl_.make_input("C2"), "cuda:0")
+    yf = torch.empty_like(xf)
+    gf = torch.ones(xf.shape[1], dtype=xf.dtype, device=xf.device)
+    bf = torch.zeros_like(gf)
+    ms = avg_ms(lambda: fk.fk_layernorm_rows(xf, yf, gf, bf), 50)
+    nb = 2 * xf.numel() * 4 + 2 * xf.shape[1] * 4
+    ln["f32_4096x1000"] = {"ms": round(ms, 5), "bytes": nb,
+                           "GBps": round(nb / (ms * 1e-3) / 1e9, 1),
+                           "note": "32 MB of traffic: launch- and latency-bound like C3"}
+    out["layernorm"] = ln
     out["chain_fused_vs_unfused"] = {
         "fused_ms": round(fused_ms, 5), "unfused_ms": round(unfused_ms, 5),
         "fused_bytes": fb, "unfused_bytes": ub,
