@@ -350,6 +350,28 @@ def measure_extras(fk, wl, torch, xs, ys, stream):
                            "GBps": round(nb / (ms * 1e-3) / 1e9, 1),
                            "note": "32 MB of traffic: launch- and latency-bound like C3"}
     out["layernorm"] = ln
+    del xf, yf
+
+    # backward kernels: bf16 GELU backward over the C5b tensor (dy = the C5b
+    # input again; two reads and one write, 6 bytes per element) and bf16
+    # softmax backward on the C4 shape (y, dy = C4 input and its softmax)
+    bw = {}
+    x5 = xs["C5b"]
+    dx5 = ys["C5b"]
+    ms = avg_ms(lambda: fk.fk_gelu_tanh_backward(x5, x5, dx5), 10)
+    nb = 3 * x5.numel() * 2
+    bw["gelu_bf16_2^30"] = {"ms": round(ms, 5), "bytes": nb,
+                            "GBps": round(nb / (ms * 1e-3) / 1e9, 1),
+                            "frac_of_peak": round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    y4 = ys["C4"]
+    dx4 = torch.empty_like(y4)
+    ms = avg_ms(lambda: fk.fk_softmax_rows_backward(y4, xs["C4"], dx4), 20)
+    nb = 3 * y4.numel() * 2
+    bw["softmax_bf16_32768x4096"] = {"ms": round(ms, 5), "bytes": nb,
+                                     "GBps": round(nb / (ms * 1e-3) / 1e9, 1),
+                                     "frac_of_peak": round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    out["backward"] = bw
+    del dx4
     out["chain_fused_vs_unfused"] = {
         "fused_ms": round(fused_ms, 5), "unfused_ms": round(unfused_ms, 5),
         "fused_bytes": fb, "unfused_bytes": ub,

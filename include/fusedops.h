@@ -187,6 +187,37 @@ int fk_layernorm_rows(const void* x, void* y, int64_t rows, int64_t cols,
 int64_t fk_layernorm_max_cols(int dtype);
 
 /*
+ * GELU backward: dx[i] = dy[i] * GELU'(x[i]) for i in [0, n), GELU' the
+ * derivative of the tanh-GELU of fk_gelu_tanh (the pages print no backward
+ * formula; this is the derivative of their forward definition):
+ * GELU'(x) = s + 2 sqrt(2/pi) x (1 + 3 * 0.044715 x^2) s (1 - s),
+ * s = 1 / (1 + exp(-2u)). Two reads and one write per element.
+ * GELU'(+inf) = 1, GELU'(-inf) = 0, NaN stays NaN. x, dy, dx: device arrays
+ * of n elements of dtype; dx may be x or dy exactly, any other overlap with
+ * them is FK_ERR_OVERLAP (x and dy may overlap each other).
+ */
+int fk_gelu_tanh_backward(const void* x, const void* dy, void* dx, int64_t n,
+                          int dtype, void* stream);
+
+/*
+ * Row softmax backward: for each row, with y the softmax output and dy the
+ * incoming gradient, dx_j = y_j (dy_j - sum_k y_k dy_k) (the product of the
+ * softmax Jacobian with dy; derived from the forward definition of
+ * fk_softmax_rows). Row strides ldy, lddy, lddx in elements, >= cols. The row
+ * is held in registers: one read of y and dy, one write of dx per element.
+ * dx may be y or dy exactly (same stride); other overlaps are
+ * FK_ERR_OVERLAP. Rows wider than fk_softmax_backward_max_cols(dtype) are
+ * FK_ERR_UNSUPPORTED.
+ */
+int fk_softmax_rows_backward(const void* y, const void* dy, void* dx,
+                             int64_t rows, int64_t cols, int64_t ldy,
+                             int64_t lddy, int64_t lddx, int dtype, void* stream);
+
+/* Widest row fk_softmax_rows_backward accepts for dtype (16384 fp32, 32768
+ * bf16), or FK_ERR_INVALID_ARG for an unknown dtype. Pure host query. */
+int64_t fk_softmax_backward_max_cols(int dtype);
+
+/*
  * Widest row (in columns) that fk_softmax_rows holds on chip for dtype, or
  * FK_ERR_INVALID_ARG for an unknown dtype. Pure host query.
  */

@@ -33,6 +33,8 @@ __all__ = [
     "fk_softmax_rows_online", "fk_softmax_rows_ws", "fk_softmax_workspace_bytes",
     "fk_set_split_wait_limit", "fk_softmax_onchip_max_cols", "fk_layernorm_rows",
     "fk_layernorm_max_cols", "fk_copy", "fk_status_string", "layernorm_rows",
+    "fk_gelu_tanh_backward", "fk_softmax_rows_backward", "fk_softmax_backward_max_cols",
+    "gelu_tanh_backward", "softmax_rows_backward",
     "gelu_tanh", "elementwise_chain", "softmax_rows",
 ]
 
@@ -79,6 +81,12 @@ def lib() -> ctypes.CDLL:
     L.fk_layernorm_rows.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp, ctypes.c_float, i32, i32,
                                     vp]
     L.fk_layernorm_rows.restype = i32
+    L.fk_gelu_tanh_backward.argtypes = [vp, vp, vp, i64, i32, vp]
+    L.fk_gelu_tanh_backward.restype = i32
+    L.fk_softmax_rows_backward.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
+    L.fk_softmax_rows_backward.restype = i32
+    L.fk_softmax_backward_max_cols.argtypes = [i32]
+    L.fk_softmax_backward_max_cols.restype = i64
     L.fk_layernorm_max_cols.argtypes = [i32]
     L.fk_layernorm_max_cols.restype = i64
     L.fk_softmax_onchip_max_cols.argtypes = [i32]
@@ -282,6 +290,34 @@ def fk_layernorm_max_cols(dtype) -> int:
     return int(v)
 
 
+def fk_gelu_tanh_backward(x, dy, dx, stream=None) -> None:
+    """dx = dy * GELU'(x) elementwise (fp32 or bf16, contiguous, same size)."""
+    n, dt = _flat_pair(x, dx, "fk_gelu_tanh_backward")
+    _flat_pair(dy, dx, "fk_gelu_tanh_backward")
+    with _torch().cuda.device(x.device):
+        _check(lib().fk_gelu_tanh_backward(x.data_ptr(), dy.data_ptr(), dx.data_ptr(), n, dt,
+                                           _stream_handle(x, stream)), "fk_gelu_tanh_backward")
+
+
+def fk_softmax_rows_backward(y, dy, dx, stream=None) -> None:
+    """dx = y * (dy - sum(y * dy)) per row of 2-D y, dy into dx (row strides honoured)."""
+    rows, cols, ldy, lddx, dt = _rows_pair(y, dx, "fk_softmax_rows_backward")
+    _, _, lddy, _, _ = _rows_pair(dy, dx, "fk_softmax_rows_backward")
+    with _torch().cuda.device(y.device):
+        _check(lib().fk_softmax_rows_backward(y.data_ptr(), dy.data_ptr(), dx.data_ptr(), rows,
+                                              cols, ldy, lddy, lddx, dt,
+                                              _stream_handle(y, stream)),
+               "fk_softmax_rows_backward")
+
+
+def fk_softmax_backward_max_cols(dtype) -> int:
+    """Widest row fk_softmax_rows_backward accepts for a torch dtype or an FK_* code."""
+    v = lib().fk_softmax_backward_max_cols(_dtype_arg(dtype))
+    if v < 0:
+        raise FusedOpsError(int(v), "fk_softmax_backward_max_cols")
+    return int(v)
+
+
 def fk_copy(x, y, nbytes: int | None = None, stream=None) -> None:
     """Copy nbytes (default: all of x) from x to y on the device."""
     _device_tensor(x, "x")
@@ -318,3 +354,15 @@ def layernorm_rows(x, gamma=None, beta=None, eps: float = 1e-5, gelu: bool = Fal
     y = _torch().empty(x.shape, dtype=x.dtype, device=x.device)
     fk_layernorm_rows(x, y, gamma, beta, eps, gelu, stream)
     return y
+
+
+def gelu_tanh_backward(x, dy, stream=None):
+    dx = _torch().empty_like(x, memory_format=_torch().contiguous_format)
+    fk_gelu_tanh_backward(x, dy, dx, stream)
+    return dx
+
+
+def softmax_rows_backward(y, dy, stream=None):
+    dx = _torch().empty(y.shape, dtype=y.dtype, device=y.device)
+    fk_softmax_rows_backward(y, dy, dx, stream)
+    return dx

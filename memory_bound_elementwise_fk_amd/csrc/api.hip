@@ -199,6 +199,37 @@ int fk_layernorm_rows(const void* x, void* y, int64_t rows, int64_t cols, int64_
                                            static_cast<hipStream_t>(stream)));
 }
 
+int fk_gelu_tanh_backward(const void* x, const void* dy, void* dx, int64_t n, int dtype,
+                          void* stream) {
+    if (!dtype_ok(dtype)) return FK_ERR_INVALID_ARG;
+    bool skip = false;
+    int st = check_flat(x, dx, n, esize(dtype), &skip);  // also: dx == x or disjoint
+    if (st != FK_OK || skip) return st;
+    st = check_flat(dy, dx, n, esize(dtype), &skip);      // dx == dy or disjoint
+    if (st != FK_OK) return st;
+    return hip_status(fk::launch_gelu_backward(x, dy, dx, n, static_cast<fk::Dtype>(dtype),
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int fk_softmax_rows_backward(const void* y, const void* dy, void* dx, int64_t rows, int64_t cols,
+                             int64_t ldy, int64_t lddy, int64_t lddx, int dtype, void* stream) {
+    bool skip = false;
+    int st = check_rows(y, dx, rows, cols, ldy, lddx, dtype, &skip);
+    if (st != FK_OK) return st;
+    st = check_rows(dy, dx, rows, cols, lddy, lddx, dtype, &skip);
+    if (st != FK_OK || skip) return st;
+    if (cols > fk::softmax_backward_max_cols(static_cast<fk::Dtype>(dtype)))
+        return FK_ERR_UNSUPPORTED;
+    return hip_status(fk::launch_softmax_backward(y, dy, dx, rows, cols, ldy, lddy, lddx,
+                                                  static_cast<fk::Dtype>(dtype),
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+int64_t fk_softmax_backward_max_cols(int dtype) {
+    if (!dtype_ok(dtype)) return FK_ERR_INVALID_ARG;
+    return fk::softmax_backward_max_cols(static_cast<fk::Dtype>(dtype));
+}
+
 int64_t fk_layernorm_max_cols(int dtype) {
     if (!dtype_ok(dtype)) return FK_ERR_INVALID_ARG;
     return fk::layernorm_max_cols(static_cast<fk::Dtype>(dtype));

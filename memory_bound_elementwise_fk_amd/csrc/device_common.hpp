@@ -156,6 +156,53 @@ __device__ inline void gelu_tanh_n(float (&v)[N]) {
     for (int j = 0; j < N; ++j) v[j] = y[j];
 }
 
+// Derivative of the tanh-GELU (for the backward pass; derived from the
+// forward definition): with s = 1 / (1 + 2^t) (the logistic of 2u) and
+// q = 1 - s, GELU'(x) = s + w s q, w = 2 sqrt(2/pi) x (1 + 3 * 0.044715 x^2).
+// q is formed without cancellation: 1 - s where s < 1/2 (t > 0), e s where
+// e = 2^t <= 1. Where s q is 0 (large |x|) the second term is dropped
+// (avoids 0 * inf), giving the limits 1 at +inf and 0 at -inf.
+constexpr float kGeluW0 = 1.5957691216057308f;    // 2 sqrt(2/pi)
+constexpr float kGeluW1 = 0.21406444881780076f;   // 6 sqrt(2/pi) 0.044715
+
+// g[j] <- g[j] * GELU'(x[j]) for N values in registers; far-negative lanes
+// (t > kGeluFarT) are patched under one wave-uniform branch as in
+// gelu_tanh_n, with s = 2^-t formed as 2^(64 - t) 2^-64.
+template <int N>
+__device__ inline void gelu_tanh_grad_n(const float (&x)[N], float (&g)[N]) {
+    float t[N];
+    float tmax = -__builtin_inff();
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        t[j] = gelu_t(x[j]);
+        tmax = fmaxf(tmax, t[j]);
+    }
+    float r[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        const float e = exp2_raw(t[j]);
+        const float s = __builtin_amdgcn_rcpf(1.0f + e);
+        const float q = t[j] > 0.0f ? 1.0f - s : e * s;
+        const float w = x[j] * fmaf(kGeluW1, x[j] * x[j], kGeluW0);
+        const float sq = s * q;
+        const float d = sq == 0.0f ? s : fmaf(w, sq, s);
+        r[j] = g[j] * d;
+    }
+    if (__builtin_amdgcn_ballot_w64(tmax > kGeluFarT) != 0) {
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            if (t[j] > kGeluFarT) {
+                const float s = exp2_raw(64.0f - t[j]);  // 2^64 GELU'-scale factor
+                const float w = x[j] * fmaf(kGeluW1, x[j] * x[j], kGeluW0);
+                const float d = s == 0.0f ? 0.0f : s * (1.0f + w);
+                r[j] = (g[j] * d) * 0x1p-64f;
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < N; ++j) g[j] = r[j];
+}
+
 // ------------------------------------------------------- wave reductions --
 // DPP lane moves within a wave64: quad_perm swaps within 4 lanes,
 // row_half_mirror reverses 8 lanes, row_mirror reverses 16 lanes. After the

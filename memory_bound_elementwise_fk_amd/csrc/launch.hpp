@@ -49,4 +49,13 @@ hipError_t launch_layernorm(const void* x, void* y, int64_t rows, int64_t cols, 
                             Dtype dt, hipStream_t s);
 int64_t layernorm_max_cols(Dtype dt);
 
+// Backward kernels: dx = dy * GELU'(x) elementwise; softmax backward
+// dx = y (dy - sum y dy) over rows of at most softmax_backward_max_cols(dt).
+hipError_t launch_gelu_backward(const void* x, const void* dy, void* dx, int64_t n, Dtype dt,
+                                hipStream_t s);
+hipError_t launch_softmax_backward(const void* y, const void* dy, void* dx, int64_t rows,
+                                   int64_t cols, int64_t ldy, int64_t lddy, int64_t lddx,
+                                   Dtype dt, hipStream_t s);
+int64_t softmax_backward_max_cols(Dtype dt);
+
 }  // namespace fk

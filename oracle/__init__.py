@@ -51,6 +51,12 @@ def _load():
         "oracle_softmax_rows_f64": ([vp, vp, i64, i64, i64, i64], i32),
         "oracle_softmax_rows_f32": ([vp, vp, i64, i64, i64, i64, i32], i32),
         "oracle_softmax_rows_bf16": ([vp, vp, i64, i64, i64, i64, i32], i32),
+        "oracle_gelu_tanh_grad_f64": ([vp, vp, i64], None),
+        "oracle_gelu_tanh_bwd_f32": ([vp, vp, vp, i64, i32], None),
+        "oracle_gelu_tanh_bwd_bf16": ([vp, vp, vp, i64, i32], None),
+        "oracle_softmax_bwd_rows_f64": ([vp, vp, vp, i64, i64], i32),
+        "oracle_softmax_bwd_rows_f32": ([vp, vp, vp, i64, i64, i32], i32),
+        "oracle_softmax_bwd_rows_bf16": ([vp, vp, vp, i64, i64, i32], i32),
         "oracle_layernorm_rows_f64": ([vp, vp, i64, i64, i64, i64, vp, vp, ctypes.c_double, i32],
                                       i32),
         "oracle_layernorm_rows_f32": ([vp, vp, i64, i64, i64, i64, vp, vp, ctypes.c_double, i32,
@@ -223,3 +229,49 @@ def layernorm_rows(x: np.ndarray, gamma: np.ndarray | None = None, beta: np.ndar
     if rc != 0:
         raise ValueError("invalid layernorm sizes or eps")
     return out
+
+
+# -------------------------------------------------------------- backward --
+def gelu_tanh_grad_f64(x: np.ndarray) -> np.ndarray:
+    """GELU'(x) of the tanh form in double, unrounded."""
+    x = _c(x, np.float64)
+    y = np.empty_like(x)
+    _load().oracle_gelu_tanh_grad_f64(_ptr(x), _ptr(y), x.size)
+    return y
+
+
+def gelu_tanh_backward(x: np.ndarray, dy: np.ndarray, threads: int = 1) -> np.ndarray:
+    """dx = dy * GELU'(x) for fp32 (float32) or bf16 (uint16) data, same dtype out."""
+    if x.shape != dy.shape or x.dtype != dy.dtype:
+        raise ValueError("x and dy must match in shape and dtype")
+    lib = _load()
+    if x.dtype == np.uint16:
+        x, dy = _c(x, np.uint16), _c(dy, np.uint16)
+        dx = np.empty_like(x)
+        lib.oracle_gelu_tanh_bwd_bf16(_ptr(x), _ptr(dy), _ptr(dx), x.size, threads)
+        return dx
+    x, dy = _c(x, np.float32), _c(dy, np.float32)
+    dx = np.empty_like(x)
+    lib.oracle_gelu_tanh_bwd_f32(_ptr(x), _ptr(dy), _ptr(dx), x.size, threads)
+    return dx
+
+
+def softmax_rows_backward(y: np.ndarray, dy: np.ndarray, threads: int = 1) -> np.ndarray:
+    """dx_j = y_j (dy_j - sum_k y_k dy_k) per row (float64, float32 or bf16 uint16)."""
+    if y.ndim != 2 or y.shape != dy.shape or y.dtype != dy.dtype:
+        raise ValueError("y and dy must be 2-D arrays of one shape and dtype")
+    rows, cols = y.shape
+    y, dy = np.ascontiguousarray(y), np.ascontiguousarray(dy)
+    dx = np.empty_like(y)
+    lib = _load()
+    if y.dtype == np.float64:
+        rc = lib.oracle_softmax_bwd_rows_f64(_ptr(y), _ptr(dy), _ptr(dx), rows, cols)
+    elif y.dtype == np.float32:
+        rc = lib.oracle_softmax_bwd_rows_f32(_ptr(y), _ptr(dy), _ptr(dx), rows, cols, threads)
+    elif y.dtype == np.uint16:
+        rc = lib.oracle_softmax_bwd_rows_bf16(_ptr(y), _ptr(dy), _ptr(dx), rows, cols, threads)
+    else:
+        raise TypeError(f"unsupported dtype {y.dtype}")
+    if rc != 0:
+        raise ValueError("invalid sizes")
+    return dx

@@ -29,6 +29,12 @@
 //    formula; the standard definition over the last axis is used: mean, the
 //    biased variance, (x - mean) / sqrt(var + eps), then gamma and beta per
 //    column, optionally followed by the tanh-GELU above.
+//  * Backward (the pages print no formulas; the P2 page names autograd
+//    integration as later work): derived from the forward definitions above.
+//    GELU'(x) = s + 2 x k (1 + 3 c x^2) s (1 - s), s = 1 / (1 + e^(-2u)),
+//    k = sqrt(2/pi), c = 0.044715, with 1 - s evaluated as 1 / (1 + e^(2u));
+//    dx = dy * GELU'(x). Softmax: dx_j = y_j (dy_j - sum_k y_k dy_k), the
+//    Jacobian-vector product of y = softmax(x).
 //
 // Readings where the pages are silent (each also listed in the design notes):
 //  * GELU(-inf) = -0 (the limit), GELU(NaN) = NaN, GELU(+inf) = +inf.
@@ -92,6 +98,21 @@ double gelu_real(double x) {
     return x / (1.0 + std::exp(-2.0 * gelu_u(x)));
 }
 
+// Derivative of the real tanh-GELU. Limits at +-inf (1 and 0); where
+// s (1 - s) underflows the second term is 0 (it avoids 0 * inf).
+double gelu_grad_real(double x) {
+    if (std::isnan(x)) return x;
+    if (x == std::numeric_limits<double>::infinity()) return 1.0;
+    if (x == -std::numeric_limits<double>::infinity()) return 0.0;
+    const double u = gelu_u(x);
+    const double s = 1.0 / (1.0 + std::exp(-2.0 * u));
+    const double q = 1.0 / (1.0 + std::exp(2.0 * u));  // 1 - s
+    const double sq = s * q;
+    if (sq == 0.0) return s;
+    const double du = kSqrt2OverPi * (1.0 + 3.0 * kCubic * x * x);
+    return s + 2.0 * x * du * sq;
+}
+
 // ---------------------------------------------------------------- chain ---
 enum OpKind { kAdd = 1, kMul = 2, kGelu = 3 };
 
@@ -149,6 +170,14 @@ void layernorm_row(const double* x, double* y, int64_t cols, const double* gamma
     }
 }
 
+// ------------------------------------------------------- softmax backward -
+// One row in double: dot = sum_k y_k dy_k; dx_j = y_j (dy_j - dot).
+void softmax_bwd_row(const double* y, const double* dy, double* dx, int64_t cols) {
+    double dot = 0.0;
+    for (int64_t j = 0; j < cols; ++j) dot += y[j] * dy[j];
+    for (int64_t j = 0; j < cols; ++j) dx[j] = y[j] * (dy[j] - dot);
+}
+
 // ---------------------------------------------------------------- threads -
 // Run body(begin, end) over [0, n) split into contiguous pieces.
 template <class Body>
@@ -202,6 +231,23 @@ void layernorm_rows_generic(const In* x, Out* y, int64_t rows, int64_t cols, int
             for (int64_t j = 0; j < cols; ++j) xin[j] = load(x[r * ldx + j]);
             layernorm_row(xin.data(), yout.data(), cols, gp, bp, eps, gelu);
             for (int64_t j = 0; j < cols; ++j) y[r * ldy + j] = store(yout[j]);
+        }
+    });
+}
+
+template <class T, class Load, class Store>
+void softmax_bwd_rows_generic(const T* y, const T* dy, T* dx, int64_t rows, int64_t cols,
+                              int nthreads, Load load, Store store) {
+    parallel_range(rows, nthreads, [&](int64_t r0, int64_t r1) {
+        std::vector<double> a(static_cast<size_t>(cols)), b(static_cast<size_t>(cols)),
+            o(static_cast<size_t>(cols));
+        for (int64_t r = r0; r < r1; ++r) {
+            for (int64_t j = 0; j < cols; ++j) {
+                a[j] = load(y[r * cols + j]);
+                b[j] = load(dy[r * cols + j]);
+            }
+            softmax_bwd_row(a.data(), b.data(), o.data(), cols);
+            for (int64_t j = 0; j < cols; ++j) dx[r * cols + j] = store(o[j]);
         }
     });
 }
@@ -290,6 +336,53 @@ int oracle_softmax_rows_bf16(const uint16_t* x, uint16_t* y, int64_t rows, int64
     softmax_rows_generic(x, y, rows, cols, ldx, ldy, nthreads,
                          [](uint16_t v) { return static_cast<double>(bf16_to_f32(v)); },
                          [](double v) { return f32_to_bf16(static_cast<float>(v)); });
+    return 0;
+}
+
+// ---- backward ----
+// GELU'(x) in double, unrounded (for the pins).
+void oracle_gelu_tanh_grad_f64(const double* x, double* y, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) y[i] = gelu_grad_real(x[i]);
+}
+// dx = dy * GELU'(x), computed in double and rounded once.
+void oracle_gelu_tanh_bwd_f32(const float* x, const float* dy, float* dx, int64_t n,
+                              int nthreads) {
+    parallel_range(n, nthreads, [&](int64_t b, int64_t e) {
+        for (int64_t i = b; i < e; ++i)
+            dx[i] = static_cast<float>(static_cast<double>(dy[i]) * gelu_grad_real(x[i]));
+    });
+}
+void oracle_gelu_tanh_bwd_bf16(const uint16_t* x, const uint16_t* dy, uint16_t* dx, int64_t n,
+                               int nthreads) {
+    parallel_range(n, nthreads, [&](int64_t b, int64_t e) {
+        for (int64_t i = b; i < e; ++i) {
+            const double g = gelu_grad_real(bf16_to_f32(x[i]));
+            dx[i] = f32_to_bf16(static_cast<float>(static_cast<double>(bf16_to_f32(dy[i])) * g));
+        }
+    });
+}
+// Softmax backward over contiguous rows (returns 0, or -1 for invalid sizes).
+int oracle_softmax_bwd_rows_f64(const double* y, const double* dy, double* dx, int64_t rows,
+                                int64_t cols) {
+    if (rows < 0 || cols < 0 || ((rows > 0 && cols > 0) && (!y || !dy || !dx))) return -1;
+    softmax_bwd_rows_generic(y, dy, dx, rows, cols, 1, [](double v) { return v; },
+                             [](double v) { return v; });
+    return 0;
+}
+int oracle_softmax_bwd_rows_f32(const float* y, const float* dy, float* dx, int64_t rows,
+                                int64_t cols, int nthreads) {
+    if (rows < 0 || cols < 0 || ((rows > 0 && cols > 0) && (!y || !dy || !dx))) return -1;
+    softmax_bwd_rows_generic(y, dy, dx, rows, cols, nthreads,
+                             [](float v) { return static_cast<double>(v); },
+                             [](double v) { return static_cast<float>(v); });
+    return 0;
+}
+int oracle_softmax_bwd_rows_bf16(const uint16_t* y, const uint16_t* dy, uint16_t* dx,
+                                 int64_t rows, int64_t cols, int nthreads) {
+    if (rows < 0 || cols < 0 || ((rows > 0 && cols > 0) && (!y || !dy || !dx))) return -1;
+    softmax_bwd_rows_generic(y, dy, dx, rows, cols, nthreads,
+                             [](uint16_t v) { return static_cast<double>(bf16_to_f32(v)); },
+                             [](double v) { return f32_to_bf16(static_cast<float>(v)); });
     return 0;
 }
 

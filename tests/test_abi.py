@@ -41,7 +41,9 @@ def test_header_declares_the_entry_points():
     for want in ("fk_gelu_tanh", "fk_elementwise_chain", "fk_softmax_rows",
                  "fk_softmax_rows_online", "fk_softmax_rows_ws", "fk_softmax_workspace_bytes",
                  "fk_set_split_wait_limit", "fk_softmax_onchip_max_cols", "fk_copy",
-                 "fk_status_string", "fk_layernorm_rows", "fk_layernorm_max_cols"):
+                 "fk_status_string", "fk_layernorm_rows", "fk_layernorm_max_cols",
+                 "fk_gelu_tanh_backward", "fk_softmax_rows_backward",
+                 "fk_softmax_backward_max_cols"):
         assert want in names
 
 
@@ -182,6 +184,32 @@ def test_layernorm_validation(L):
     assert ln(A, B, 4, 10, 10, 10, B + 8, None, 1e-5, 0, 0, None) == fk.FK_ERR_OVERLAP
     assert ln(A, B, 4, 10, 10, 10, G, B + 100, 1e-5, 0, 0, None) == fk.FK_ERR_OVERLAP
     assert ln(A, A + 8, 4, 10, 10, 10, None, None, 1e-5, 0, 0, None) == fk.FK_ERR_OVERLAP
+
+
+def test_backward_validation(L):
+    gb = L.fk_gelu_tanh_backward
+    C = 0x7F0000A00000
+    assert gb(A, B, C, 0, 0, None) == fk.FK_OK
+    assert gb(None, B, C, 5, 0, None) == fk.FK_ERR_INVALID_ARG
+    assert gb(A, None, C, 5, 0, None) == fk.FK_ERR_INVALID_ARG
+    assert gb(A, B, None, 5, 0, None) == fk.FK_ERR_INVALID_ARG
+    assert gb(A, B, C, -5, 0, None) == fk.FK_ERR_INVALID_ARG
+    assert gb(A, B, C, 5, 4, None) == fk.FK_ERR_INVALID_ARG
+    assert gb(A, B, A + 4, 5, 0, None) == fk.FK_ERR_OVERLAP       # dx partly over x
+    assert gb(A, B, B + 8, 5, 0, None) == fk.FK_ERR_OVERLAP       # dx partly over dy
+    sb = L.fk_softmax_rows_backward
+    assert L.fk_softmax_backward_max_cols(fk.FK_F32) == 16384
+    assert L.fk_softmax_backward_max_cols(fk.FK_BF16) == 32768
+    assert L.fk_softmax_backward_max_cols(3) == fk.FK_ERR_INVALID_ARG
+    assert sb(A, B, C, 0, 10, 10, 10, 10, 0, None) == fk.FK_OK
+    assert sb(A, B, C, 4, 10, 9, 10, 10, 0, None) == fk.FK_ERR_INVALID_ARG
+    assert sb(A, B, C, 4, 10, 10, 9, 10, 0, None) == fk.FK_ERR_INVALID_ARG
+    assert sb(A, B, C, 4, 10, 10, 10, 9, 0, None) == fk.FK_ERR_INVALID_ARG
+    assert sb(A, None, C, 4, 10, 10, 10, 10, 0, None) == fk.FK_ERR_INVALID_ARG
+    assert sb(A, B, A + 40, 4, 10, 10, 10, 10, 0, None) == fk.FK_ERR_OVERLAP
+    assert sb(A, B, B, 4, 10, 10, 12, 10, 0, None) == fk.FK_ERR_OVERLAP   # in place, other stride
+    assert sb(A, B, C, 2, 16385, 16385, 16385, 16385, 0, None) == fk.FK_ERR_UNSUPPORTED
+    assert sb(A, B, C, 2, 32769, 32769, 32769, 32769, 1, None) == fk.FK_ERR_UNSUPPORTED
 
 
 def test_copy_validation(L):
