@@ -33,6 +33,7 @@ ROOT = Path(__file__).resolve().parent
 sys.path.insert(0, str(ROOT))
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 STEP = ("C3", "C4", "C5a", "C5b")
 TRAFFIC_FILE = ROOT / "profiles" / "traffic.json"
 KERNEL_SOURCES = ("device_common.hpp", "ew_kernels.hpp", "softmax_kernels.hpp", "elementwise.hip",
@@ -372,6 +373,28 @@ def measure_extras(fk, wl, torch, xs, ys, stream):
                                      "frac_of_peak": round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     out["backward"] = bw
     del dx4
+
+    # Linear + GELU on the matrix cores (MLP up-projection: 8192 tokens,
+    # 4096 -> 16384 features, bf16), against torch's library matmul
+    # (hipBLASLt) alone and followed by a separate GELU kernel
+    M, N, K = 8192, 16384, 4096
+    xl = wl_.to_torch(wl_.draw(M * K, seed=3, dtype="bf16"), "cuda:0").view(M, K)
+    wlin = wl_.to_torch(wl_.draw(N * K, seed=4, scale=K ** -0.5, dtype="bf16"), "cuda:0").view(N, K)
+    bl = wl_.to_torch(wl_.draw(N, seed=5, dtype="bf16"), "cuda:0")
+    yl = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+    flops = 2.0 * M * N * K
+    fused = avg_ms(lambda: fk.fk_linear_gelu(xl, wlin, bl, yl), 10)
+    lib_mm = avg_ms(lambda: torch.nn.functional.linear(xl, wlin, bl), 10)
+    lib_unfused = avg_ms(lambda: torch.nn.functional.gelu(torch.nn.functional.linear(xl, wlin, bl),
+                                                          approximate="tanh"), 10)
+    out["linear_gelu"] = {
+        "shape": [M, N, K], "fused_ms": round(fused, 4),
+        "fused_TFLOPs": round(flops / (fused * 1e-3) / 1e12, 1),
+        "frac_of_mfma_peak": round(flops / (fused * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "library_linear_ms": round(lib_mm, 4),
+        "library_linear_then_gelu_ms": round(lib_unfused, 4),
+        "note": "library = torch.nn.functional.linear (hipBLASLt) and its separate GELU"}
+    del xl, wlin, bl, yl
     out["chain_fused_vs_unfused"] = {
         "fused_ms": round(fused_ms, 5), "unfused_ms": round(unfused_ms, 5),
         "fused_bytes": fb, "unfused_bytes": ub,

@@ -218,6 +218,25 @@ int fk_softmax_rows_backward(const void* y, const void* dy, void* dx,
 int64_t fk_softmax_backward_max_cols(int dtype);
 
 /*
+ * Linear layer with a fused GELU epilogue on the matrix cores:
+ * y[i][j] = GELU(sum_k x[i][k] w[j][k] + bias[j]) (or without GELU when
+ * fuse_gelu is 0), i < M, j < N: the Linear -> GELU part of the LayerNorm ->
+ * Linear -> GELU fusion example of "Lecture 6: GPU Kernels and Triton",
+ * section 6.1, with the activation applied to the fp32 accumulators instead
+ * of a second pass over the M x N product. x: M rows of K (row stride ldx),
+ * w: N rows of K (a Linear weight, row stride ldw), bias: N values or NULL,
+ * y: M rows of N (row stride ldy); all DEVICE memory of dtype. fp32
+ * accumulation; y rounded once to bf16 (nearest even).
+ * Supported: dtype FK_BF16 only; K, ldx and ldw multiples of 8; x and w
+ * 16-byte aligned -- else FK_ERR_UNSUPPORTED. y must not overlap x, w or
+ * bias (FK_ERR_OVERLAP). M == 0 or N == 0: nothing to do. K == 0 gives
+ * GELU(bias).
+ */
+int fk_linear_gelu(const void* x, const void* w, const void* bias, void* y,
+                   int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldw,
+                   int64_t ldy, int fuse_gelu, int dtype, void* stream);
+
+/*
  * Widest row (in columns) that fk_softmax_rows holds on chip for dtype, or
  * FK_ERR_INVALID_ARG for an unknown dtype. Pure host query.
  */

@@ -34,7 +34,7 @@ __all__ = [
     "fk_set_split_wait_limit", "fk_softmax_onchip_max_cols", "fk_layernorm_rows",
     "fk_layernorm_max_cols", "fk_copy", "fk_status_string", "layernorm_rows",
     "fk_gelu_tanh_backward", "fk_softmax_rows_backward", "fk_softmax_backward_max_cols",
-    "gelu_tanh_backward", "softmax_rows_backward",
+    "gelu_tanh_backward", "softmax_rows_backward", "fk_linear_gelu", "linear_gelu",
     "gelu_tanh", "elementwise_chain", "softmax_rows",
 ]
 
@@ -87,6 +87,8 @@ def lib() -> ctypes.CDLL:
     L.fk_softmax_rows_backward.restype = i32
     L.fk_softmax_backward_max_cols.argtypes = [i32]
     L.fk_softmax_backward_max_cols.restype = i64
+    L.fk_linear_gelu.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, i32, vp]
+    L.fk_linear_gelu.restype = i32
     L.fk_layernorm_max_cols.argtypes = [i32]
     L.fk_layernorm_max_cols.restype = i64
     L.fk_softmax_onchip_max_cols.argtypes = [i32]
@@ -318,6 +320,31 @@ def fk_softmax_backward_max_cols(dtype) -> int:
     return int(v)
 
 
+def fk_linear_gelu(x, w, bias, y, gelu: bool = True, stream=None) -> None:
+    """y = GELU(x @ w.T + bias) for 2-D bf16 x [M, K], w [N, K], bias [N] or None, y [M, N]."""
+    for t, name in ((x, "x"), (w, "w"), (y, "y")):
+        _device_tensor(t, name)
+        if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+            raise ValueError(f"fk_linear_gelu: {name} must be 2-D with contiguous rows")
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K or tuple(y.shape) != (M, N):
+        raise ValueError("fk_linear_gelu: shapes x [M, K], w [N, K], y [M, N] do not match")
+    if x.dtype != w.dtype or x.dtype != y.dtype:
+        raise TypeError("fk_linear_gelu: x, w and y must share a dtype")
+    b = None
+    if bias is not None:
+        _device_tensor(bias, "bias")
+        if bias.dtype != x.dtype or bias.dim() != 1 or bias.numel() != N or not bias.is_contiguous():
+            raise ValueError("fk_linear_gelu: bias must be a contiguous [N] tensor of x's dtype")
+        b = bias.data_ptr()
+    ld = lambda t, n: t.stride(0) if t.shape[0] > 1 else n  # noqa: E731
+    with _torch().cuda.device(x.device):
+        _check(lib().fk_linear_gelu(x.data_ptr(), w.data_ptr(), b, y.data_ptr(), M, N, K,
+                                    ld(x, K), ld(w, K), ld(y, N), int(bool(gelu)),
+                                    _dtype_code(x), _stream_handle(x, stream)), "fk_linear_gelu")
+
+
 def fk_copy(x, y, nbytes: int | None = None, stream=None) -> None:
     """Copy nbytes (default: all of x) from x to y on the device."""
     _device_tensor(x, "x")
@@ -366,3 +393,9 @@ def softmax_rows_backward(y, dy, stream=None):
     dx = _torch().empty(y.shape, dtype=y.dtype, device=y.device)
     fk_softmax_rows_backward(y, dy, dx, stream)
     return dx
+
+
+def linear_gelu(x, w, bias=None, gelu: bool = True, stream=None):
+    y = _torch().empty((x.shape[0], w.shape[0]), dtype=x.dtype, device=x.device)
+    fk_linear_gelu(x, w, bias, y, gelu, stream)
+    return y

@@ -230,6 +230,33 @@ int64_t fk_softmax_backward_max_cols(int dtype) {
     return fk::softmax_backward_max_cols(static_cast<fk::Dtype>(dtype));
 }
 
+int fk_linear_gelu(const void* x, const void* w, const void* bias, void* y, int64_t M, int64_t N,
+                   int64_t K, int64_t ldx, int64_t ldw, int64_t ldy, int fuse_gelu, int dtype,
+                   void* stream) {
+    if (!dtype_ok(dtype)) return FK_ERR_INVALID_ARG;
+    if (M < 0 || N < 0 || K < 0) return FK_ERR_INVALID_ARG;
+    if (fuse_gelu != 0 && fuse_gelu != 1) return FK_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return FK_OK;
+    if (y == nullptr || (K > 0 && (x == nullptr || w == nullptr))) return FK_ERR_INVALID_ARG;
+    if (ldy < N || (K > 0 && (ldx < K || ldw < K))) return FK_ERR_INVALID_ARG;
+    if (dtype != FK_BF16) return FK_ERR_UNSUPPORTED;
+    // x and w are read only when K > 0 (K == 0 gives GELU(bias))
+    if (K > 0 && (K % 8 != 0 || ldx % 8 != 0 || ldw % 8 != 0 ||
+                  ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w)) & 15u) != 0))
+        return FK_ERR_UNSUPPORTED;
+    if (fk::linear_tiles(M, N) > fk::linear_max_tiles()) return FK_ERR_UNSUPPORTED;
+    if (M - 1 > (kI64Max / 2 - N) / ldy || (K > 0 && (M - 1 > (kI64Max / 2 - K) / ldx ||
+                                                     N - 1 > (kI64Max / 2 - K) / ldw)))
+        return FK_ERR_UNSUPPORTED;
+    const int64_t by = ((M - 1) * ldy + N) * 2;
+    if (K > 0 && (ranges_overlap(y, by, x, ((M - 1) * ldx + K) * 2) ||
+                  ranges_overlap(y, by, w, ((N - 1) * ldw + K) * 2)))
+        return FK_ERR_OVERLAP;
+    if (bias != nullptr && ranges_overlap(y, by, bias, N * 2)) return FK_ERR_OVERLAP;
+    return hip_status(fk::launch_linear_gelu(x, w, bias, y, M, N, K, ldx, ldw, ldy, fuse_gelu,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 int64_t fk_layernorm_max_cols(int dtype) {
     if (!dtype_ok(dtype)) return FK_ERR_INVALID_ARG;
     return fk::layernorm_max_cols(static_cast<fk::Dtype>(dtype));

@@ -1,0 +1,203 @@
+// gemm_kernels.hpp -- Linear layer with a fused GELU epilogue on the gfx950
+// matrix cores: Y = GELU(X W^T + b), X [M, K], W [N, K] (a Linear weight:
+// one row per output feature), b [N], Y [M, N], bf16 in and out, fp32
+// accumulation.
+//
+// This is the Linear -> GELU part of the LayerNorm -> Linear -> GELU fusion
+// example of "Lecture 6: GPU Kernels and Triton", section 6.1: the product
+// is a dense contraction (compute-bound, section 5), so it runs on MFMA, and
+// the activation is applied to the accumulators in registers instead of a
+// second kernel that would read and write the M x N product again. The
+// tiling follows the same idea as that page's blocked matmul (section 5.1:
+// tiles of the output, a K loop over tiles of the operands staged on chip,
+// an fp32 accumulator), built here for 64-wide waves and MFMA tiles.
+//
+// Block tile BM x BN, K step BK; the block's waves form a (BM/WM) x (BN/WN)
+// grid, each computing a WM x WN tile as (WM/32) x (WN/32) MFMA 32x32x16
+// tiles. Operand tiles are staged through LDS, double-buffered: the global
+// loads of step k+1 are in flight while step k is multiplied, and one
+// barrier per step separates the buffers. LDS rows are padded by 16 bytes
+// so the 16-byte fragment reads of 32 consecutive rows do not pile onto the
+// same banks.
+//
+// MFMA 32x32x16 bf16 operand layout (checked on the device): lane l supplies
+// A row l % 32 and B column l % 32, each at k = (l / 32) * 8 + e for its 8
+// values e; accumulator value v of lane l is C[(v / 4) * 8 + (l / 32) * 4 +
+// v % 4][l % 32].
+#pragma once
+
+#include "device_common.hpp"
+
+namespace fk {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <int BM_, int BN_, int BK_, int WM_, int WN_>
+struct GemmShape {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
+    static constexpr int kWavesM = BM / WM, kWavesN = BN / WN;
+    static constexpr int kThreads = kWavesM * kWavesN * kWave;
+    static constexpr int kTM = WM / 32, kTN = WN / 32;
+    static constexpr int kStride = BK + 8;           // bf16 per LDS row (16 bytes of padding)
+    static constexpr int kChunksPerRow = BK / 8;     // 16-byte chunks per operand row
+    static constexpr int kLoadsA = BM * kChunksPerRow / kThreads;
+    static constexpr int kLoadsB = BN * kChunksPerRow / kThreads;
+    static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "tiles");
+    static_assert(BK % 16 == 0, "K step");
+    static_assert(BM * kChunksPerRow % kThreads == 0 && BN * kChunksPerRow % kThreads == 0,
+                  "every thread loads whole chunks");
+};
+
+// Block index -> output tile (tm, tn). Blocks go to the 8 XCDs round-robin
+// (block b on XCD b % 8); when the block count divides by 8 the index is
+// first remapped so that each XCD works through a contiguous range of the
+// ordering below, then tiles are visited in column-strips of kGroup tile
+// rows, so the blocks in flight on one XCD share operand tiles in its L2.
+constexpr int kGemmGroup = 16;
+constexpr int kXcds = 8;
+
+__device__ inline void gemm_tile_of(int64_t b, int64_t tiles_m, int64_t tiles_n, int64_t& tm,
+                                    int64_t& tn) {
+    const int64_t nb = tiles_m * tiles_n;
+    if (nb % kXcds == 0) b = (b % kXcds) * (nb / kXcds) + b / kXcds;
+    const int64_t per_group = int64_t(kGemmGroup) * tiles_n;
+    const int64_t g = b / per_group;
+    const int64_t first = g * kGemmGroup;
+    const int64_t rows = tiles_m - first < kGemmGroup ? tiles_m - first : kGemmGroup;
+    const int64_t r = b - g * per_group;
+    tm = first + r % rows;
+    tn = r / rows;
+}
+
+template <class S>
+__global__ __launch_bounds__(S::kThreads) void linear_gelu_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K,
+    int64_t ldx, int64_t ldw, int64_t ldy, int gelu) {
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][S::BM * S::kStride];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][S::BN * S::kStride];
+
+    const int64_t tiles_m = (M + S::BM - 1) / S::BM;
+    const int64_t tiles_n = (N + S::BN - 1) / S::BN;
+    int64_t tm, tn;
+    gemm_tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int64_t m0 = tm * S::BM, n0 = tn * S::BN;
+
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int wave = tid / kWave;
+    const int wm = wave / S::kWavesN, wn = wave % S::kWavesN;
+
+    // this thread's 16-byte chunks of the operand tiles (row, k offset); a
+    // step whose tiles lie wholly inside X and W (a uniform test: all but the
+    // edge tiles) loads without masks, so all loads are in flight together
+    const bool inner_mn = m0 + S::BM <= M && n0 + S::BN <= N;
+    u32x4 ra[S::kLoadsA], rb[S::kLoadsB];
+    auto load_tiles = [&](int64_t k0) {
+        if (inner_mn && k0 + S::BK <= K) {
+#pragma unroll
+            for (int i = 0; i < S::kLoadsA; ++i) {
+                const int c = tid + i * S::kThreads;
+                ra[i] = *reinterpret_cast<const u32x4*>(X + (m0 + c / S::kChunksPerRow) * ldx + k0 +
+                                                        (c % S::kChunksPerRow) * 8);
+            }
+#pragma unroll
+            for (int i = 0; i < S::kLoadsB; ++i) {
+                const int c = tid + i * S::kThreads;
+                rb[i] = *reinterpret_cast<const u32x4*>(W + (n0 + c / S::kChunksPerRow) * ldw + k0 +
+                                                        (c % S::kChunksPerRow) * 8);
+            }
+            return;
+        }
+#pragma unroll
+        for (int i = 0; i < S::kLoadsA; ++i) {
+            const int c = tid + i * S::kThreads;
+            const int64_t row = m0 + c / S::kChunksPerRow;
+            const int64_t k = k0 + (c % S::kChunksPerRow) * 8;
+            ra[i] = (row < M && k < K) ? *reinterpret_cast<const u32x4*>(X + row * ldx + k)
+                                       : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int i = 0; i < S::kLoadsB; ++i) {
+            const int c = tid + i * S::kThreads;
+            const int64_t row = n0 + c / S::kChunksPerRow;
+            const int64_t k = k0 + (c % S::kChunksPerRow) * 8;
+            rb[i] = (row < N && k < K) ? *reinterpret_cast<const u32x4*>(W + row * ldw + k)
+                                       : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto store_tiles = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < S::kLoadsA; ++i) {
+            const int c = tid + i * S::kThreads;
+            *reinterpret_cast<u32x4*>(&As[buf][(c / S::kChunksPerRow) * S::kStride +
+                                               (c % S::kChunksPerRow) * 8]) = ra[i];
+        }
+#pragma unroll
+        for (int i = 0; i < S::kLoadsB; ++i) {
+            const int c = tid + i * S::kThreads;
+            *reinterpret_cast<u32x4*>(&Bs[buf][(c / S::kChunksPerRow) * S::kStride +
+                                               (c % S::kChunksPerRow) * 8]) = rb[i];
+        }
+    };
+
+    f32x16 acc[S::kTM][S::kTN];
+#pragma unroll
+    for (int i = 0; i < S::kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < S::kTN; ++j) acc[i][j] = f32x16{};
+
+    const int64_t nk = (K + S::BK - 1) / S::BK;
+    load_tiles(0);
+    store_tiles(0);
+    __syncthreads();
+    const int frag_row = lane % 32;
+    const int frag_k = (lane / 32) * 8;
+    for (int64_t kt = 0; kt < nk; ++kt) {
+        const int buf = static_cast<int>(kt & 1);
+        if (kt + 1 < nk) load_tiles((kt + 1) * S::BK);
+        const uint16_t* a_base = &As[buf][(wm * S::WM + frag_row) * S::kStride + frag_k];
+        const uint16_t* b_base = &Bs[buf][(wn * S::WN + frag_row) * S::kStride + frag_k];
+#pragma unroll
+        for (int kk = 0; kk < S::BK / 16; ++kk) {
+            bf16x8 af[S::kTM], bf[S::kTN];
+#pragma unroll
+            for (int i = 0; i < S::kTM; ++i)
+                af[i] = *reinterpret_cast<const bf16x8*>(a_base + i * 32 * S::kStride + kk * 16);
+#pragma unroll
+            for (int j = 0; j < S::kTN; ++j)
+                bf[j] = *reinterpret_cast<const bf16x8*>(b_base + j * 32 * S::kStride + kk * 16);
+#pragma unroll
+            for (int i = 0; i < S::kTM; ++i)
+#pragma unroll
+                for (int j = 0; j < S::kTN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j],
+                                                                        0, 0, 0);
+        }
+        if (kt + 1 < nk) store_tiles(buf ^ 1);
+        __syncthreads();
+    }
+
+    // epilogue: + bias, GELU on the accumulators, round to bf16, store
+#pragma unroll
+    for (int j = 0; j < S::kTN; ++j) {
+        const int64_t col = n0 + wn * S::WN + j * 32 + lane % 32;
+        const float bv = (bias != nullptr && col < N) ? IoBF16::load1(bias, col) : 0.0f;
+#pragma unroll
+        for (int i = 0; i < S::kTM; ++i) {
+            float v[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) v[e] = acc[i][j][e] + bv;
+            if (gelu) gelu_tanh_n(v);
+            const int64_t row0 = m0 + wm * S::WM + i * 32 + (lane / 32) * 4;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int64_t row = row0 + (e / 4) * 8 + e % 4;
+                if (row < M && col < N) IoBF16::store1(Y, row * ldy + col, v[e]);
+            }
+        }
+    }
+}
+
+}  // namespace fk

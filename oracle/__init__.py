@@ -275,3 +275,35 @@ def softmax_rows_backward(y: np.ndarray, dy: np.ndarray, threads: int = 1) -> np
     if rc != 0:
         raise ValueError("invalid sizes")
     return dx
+
+
+# ------------------------------------------------------ linear + GELU -----
+def _as_f64(a: np.ndarray) -> np.ndarray:
+    return bf16_to_f32(a).astype(np.float64) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
+def linear_gelu(x: np.ndarray, w: np.ndarray, bias: np.ndarray | None = None, gelu: bool = True,
+                rows: np.ndarray | None = None) -> np.ndarray:
+    """y = GELU(x w^T + bias) in double, rounded once to x's storage type.
+
+    x [M, K], w [N, K], bias [N] (float32, or bf16 as uint16 bits). The
+    product is numpy's float64 matmul of the stored values (a library
+    primitive used as one step); the bias is added in double, GELU is the
+    oracle's real tanh-GELU; the result is rounded to fp32 and, for bf16
+    data, then to bf16. ``rows`` selects a subset of rows of x (sampling).
+    """
+    xd = _as_f64(x if rows is None else x[np.asarray(rows)])
+    wd = _as_f64(w)
+    acc = xd @ wd.T
+    if bias is not None:
+        acc = acc + _as_f64(bias)[None, :]
+    if gelu:
+        acc = gelu_tanh_f64(acc).reshape(acc.shape)
+    out = acc.astype(np.float32)
+    return f32_to_bf16(out).reshape(out.shape) if x.dtype == np.uint16 else out
+
+
+def linear_abs_bound(x: np.ndarray, w: np.ndarray, rows: np.ndarray | None = None) -> np.ndarray:
+    """(|x| |w|^T)_ij in double: the scale of the accumulation error bounds."""
+    xd = np.abs(_as_f64(x if rows is None else x[np.asarray(rows)]))
+    return xd @ np.abs(_as_f64(w)).T

@@ -43,7 +43,7 @@ def test_header_declares_the_entry_points():
                  "fk_set_split_wait_limit", "fk_softmax_onchip_max_cols", "fk_copy",
                  "fk_status_string", "fk_layernorm_rows", "fk_layernorm_max_cols",
                  "fk_gelu_tanh_backward", "fk_softmax_rows_backward",
-                 "fk_softmax_backward_max_cols"):
+                 "fk_softmax_backward_max_cols", "fk_linear_gelu"):
         assert want in names
 
 
@@ -210,6 +210,27 @@ def test_backward_validation(L):
     assert sb(A, B, B, 4, 10, 10, 12, 10, 0, None) == fk.FK_ERR_OVERLAP   # in place, other stride
     assert sb(A, B, C, 2, 16385, 16385, 16385, 16385, 0, None) == fk.FK_ERR_UNSUPPORTED
     assert sb(A, B, C, 2, 32769, 32769, 32769, 32769, 1, None) == fk.FK_ERR_UNSUPPORTED
+
+
+def test_linear_validation(L):
+    f = L.fk_linear_gelu
+    Y = 0x7F0000B00000
+    bf = fk.FK_BF16
+    assert f(A, B, None, Y, 0, 10, 16, 16, 16, 10, 1, bf, None) == fk.FK_OK      # M == 0
+    assert f(A, B, None, Y, 4, 0, 16, 16, 16, 10, 1, bf, None) == fk.FK_OK      # N == 0
+    assert f(A, B, None, Y, -1, 10, 16, 16, 16, 10, 1, bf, None) == fk.FK_ERR_INVALID_ARG
+    assert f(A, B, None, Y, 4, 10, 16, 16, 16, 10, 2, bf, None) == fk.FK_ERR_INVALID_ARG
+    assert f(A, B, None, Y, 4, 10, 16, 16, 16, 10, 1, 9, None) == fk.FK_ERR_INVALID_ARG
+    assert f(A, B, None, None, 4, 10, 16, 16, 16, 10, 1, bf, None) == fk.FK_ERR_INVALID_ARG
+    assert f(None, B, None, Y, 4, 10, 16, 16, 16, 10, 1, bf, None) == fk.FK_ERR_INVALID_ARG
+    assert f(A, B, None, Y, 4, 10, 16, 8, 16, 10, 1, bf, None) == fk.FK_ERR_INVALID_ARG  # ldx < K
+    assert f(A, B, None, Y, 4, 10, 16, 16, 16, 9, 1, bf, None) == fk.FK_ERR_INVALID_ARG  # ldy < N
+    assert f(A, B, None, Y, 4, 10, 16, 16, 16, 10, 1, fk.FK_F32, None) == fk.FK_ERR_UNSUPPORTED
+    assert f(A, B, None, Y, 4, 10, 12, 16, 16, 10, 1, bf, None) == fk.FK_ERR_UNSUPPORTED  # K % 8
+    assert f(A, B, None, Y, 4, 10, 16, 20, 16, 10, 1, bf, None) == fk.FK_ERR_UNSUPPORTED  # ldx % 8
+    assert f(A + 2, B, None, Y, 4, 10, 16, 16, 16, 10, 1, bf, None) == fk.FK_ERR_UNSUPPORTED
+    assert f(A, B, None, A + 32, 4, 10, 16, 16, 16, 10, 1, bf, None) == fk.FK_ERR_OVERLAP
+    assert f(A, B, Y + 4, Y, 4, 10, 16, 16, 16, 10, 1, bf, None) == fk.FK_ERR_OVERLAP
 
 
 def test_copy_validation(L):

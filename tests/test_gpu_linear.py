@@ -1,0 +1,104 @@
+"""GPU parity of the Linear + GELU kernel (MFMA) against the CPU oracle.
+Needs an MI355X.
+
+Tolerance (derived from the arithmetic; the pages and the benchmark spec fix
+none for the matmul): the kernel accumulates the K products in fp32 in an
+order the matrix cores choose, so any summation order must pass:
+|y - r| <= ulp_bf16(|r|) + 1.13 (K + 2) 2^-24 ((|x| |w|^T)_ij + |b_j|)
+(the rounding of y to bf16, plus the worst-case fp32 accumulation error,
+through GELU's slope <= 1.13). As a sharper statistical check, at least
+99 % of the outputs must be within one bf16 ulp of the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import memory_bound_elementwise_fk_amd as fk
+import oracle
+from memory_bound_elementwise_fk_amd import workloads as wl
+from tests.gpu_util import DEV, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def bf16_ulp(r):
+    e = np.floor(np.log2(np.maximum(np.abs(r), 2.0 ** -126)))
+    return np.exp2(e - 7)
+
+
+def operands(M, N, K, seed, bias=True):
+    rng = np.random.default_rng(seed)
+    x = wl.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32)).reshape(M, K)
+    w = wl.f32_to_bf16_bits((rng.standard_normal((N, K)) / np.sqrt(max(K, 1)))
+                            .astype(np.float32)).reshape(N, K)
+    b = wl.f32_to_bf16_bits(rng.standard_normal(N).astype(np.float32)) if bias else None
+    return x, w, b
+
+
+def check(got, x, w, b, gelu, what, rows=None):
+    ref = oracle.linear_gelu(x, w, b, gelu=gelu, rows=rows)
+    g = oracle.bf16_to_f32(got).astype(np.float64)
+    r = oracle.bf16_to_f32(ref).astype(np.float64)
+    K = x.shape[1]
+    scale = oracle.linear_abs_bound(x, w, rows=rows)
+    if b is not None:
+        scale = scale + np.abs(oracle.bf16_to_f32(b).astype(np.float64))[None, :]
+    lim = bf16_ulp(r) + 1.13 * (K + 2) * 2.0 ** -24 * scale
+    err = np.abs(g - r)
+    bad = np.flatnonzero(err > lim)
+    assert bad.size == 0, f"{what}: {bad.size} beyond the bound, worst excess {(err - lim).max():.3e}"
+    within = np.mean(err <= bf16_ulp(r))
+    assert within >= 0.99, f"{what}: only {within:.4f} of outputs within one bf16 ulp"
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 8), (7, 13, 24), (300, 200, 392), (256, 256, 64),
+                                   (257, 511, 520), (512, 768, 1024), (1000, 300, 8)])
+@pytest.mark.parametrize("gelu", [True, False])
+def test_linear_shapes(M, N, K, gelu):
+    x, w, b = operands(M, N, K, seed=M * 7 + N + K)
+    y = fk.linear_gelu(to_dev(x), to_dev(w), to_dev(b), gelu=gelu)
+    check(to_host(y), x, w, b, gelu, f"{M}x{N}x{K} gelu={gelu}")
+
+
+def test_linear_without_bias_and_k_zero():
+    x, w, _ = operands(130, 70, 40, seed=3, bias=False)
+    y = fk.linear_gelu(to_dev(x), to_dev(w), None)
+    check(to_host(y), x, w, None, True, "no bias")
+    # K == 0: the product is empty, y = GELU(bias)
+    b = wl.f32_to_bf16_bits(np.linspace(-3, 3, 70).astype(np.float32))
+    xe = torch.empty((5, 0), dtype=torch.bfloat16, device=DEV)
+    we = torch.empty((70, 0), dtype=torch.bfloat16, device=DEV)
+    ye = fk.linear_gelu(xe, we, to_dev(b))
+    assert np.array_equal(to_host(ye), np.broadcast_to(oracle.gelu_tanh(b), (5, 70)))
+
+
+def test_linear_strided_operands():
+    M, N, K = 300, 260, 136
+    x, w, b = operands(M, N, K, seed=5)
+    xb = np.zeros((M, K + 8), np.uint16)
+    xb[:, :K] = x
+    wb = np.zeros((N, K + 16), np.uint16)
+    wb[:, :K] = w
+    ybuf = torch.full((M, N + 3), 0x7FC1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    fk.fk_linear_gelu(to_dev(xb)[:, :K], to_dev(wb)[:, :K], to_dev(b), ybuf[:, :N])
+    got = to_host(ybuf)
+    check(got[:, :N], x, w, b, True, "strided")
+    assert np.all(got[:, N:] == 0x7FC1), "row padding of y was written"
+
+
+def test_linear_mlp_shape_sampled_rows():
+    # the MLP up-projection shape the bench times: 8192 x 4096 -> 16384
+    M, N, K = 8192, 16384, 4096
+    x, w, b = operands(M, N, K, seed=9)
+    y = fk.linear_gelu(to_dev(x), to_dev(w), to_dev(b))
+    rows = np.sort(np.random.default_rng(10).choice(M, 48, replace=False))
+    got = to_host(y[torch.from_numpy(rows).to(DEV)])
+    check(got, x, w, b, True, "8192x16384x4096 sampled rows", rows=rows)
+
+
+def test_linear_is_bitwise_reproducible():
+    x, w, b = operands(512, 512, 512, seed=12)
+    xt, wt, bt = to_dev(x), to_dev(w), to_dev(b)
+    a = fk.linear_gelu(xt, wt, bt)
+    c = fk.linear_gelu(xt, wt, bt)
+    assert torch.equal(a.view(torch.int16), c.view(torch.int16))
