@@ -237,6 +237,27 @@ int fk_linear_gelu(const void* x, const void* w, const void* bias, void* y,
                    int64_t ldy, int fuse_gelu, int dtype, void* stream);
 
 /*
+ * FlashAttention forward: for every batch b < B and head h < H,
+ * O = softmax(Q K^T / sqrt(d) + mask) V over T positions, without forming
+ * the T x T scores in HBM ("Lecture 6: GPU Kernels and Triton", sections
+ * 7.3 and 8: blocks of queries against blocks of keys, online softmax with
+ * a running max, sum and output accumulator, one division at the end).
+ * causal = 1 keeps key j for query i when j <= i; causal = 0 keeps all.
+ * q, k, v, o: DEVICE tensors [B, H, T, d] of dtype addressed by strides
+ * (host array of 12 element strides: batch, head and row stride of q, then
+ * of k, v, o; the d values of a row are contiguous). fp32 statistics and
+ * accumulators; P is rounded to bf16 before the P V product (as the page's
+ * kernel rounds P to V's dtype); O rounded once to bf16.
+ * Supported: dtype FK_BF16, d == 128, 16-byte aligned bases, strides that
+ * are multiples of 8, B * H <= 65535 -- else FK_ERR_UNSUPPORTED. o must not
+ * overlap q, k or v (FK_ERR_OVERLAP). B, H or T == 0: nothing to do.
+ */
+int fk_attention_fwd(const void* q, const void* k, const void* v, void* o,
+                     int64_t B, int64_t H, int64_t T, int64_t d,
+                     const int64_t* strides, int causal, int dtype,
+                     void* stream);
+
+/*
  * Widest row (in columns) that fk_softmax_rows holds on chip for dtype, or
  * FK_ERR_INVALID_ARG for an unknown dtype. Pure host query.
  */

@@ -35,6 +35,7 @@ __all__ = [
     "fk_layernorm_max_cols", "fk_copy", "fk_status_string", "layernorm_rows",
     "fk_gelu_tanh_backward", "fk_softmax_rows_backward", "fk_softmax_backward_max_cols",
     "gelu_tanh_backward", "softmax_rows_backward", "fk_linear_gelu", "linear_gelu",
+    "fk_attention_fwd", "attention_fwd",
     "gelu_tanh", "elementwise_chain", "softmax_rows",
 ]
 
@@ -89,6 +90,9 @@ def lib() -> ctypes.CDLL:
     L.fk_softmax_backward_max_cols.restype = i64
     L.fk_linear_gelu.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, i32, vp]
     L.fk_linear_gelu.restype = i32
+    L.fk_attention_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ctypes.POINTER(i64), i32,
+                                   i32, vp]
+    L.fk_attention_fwd.restype = i32
     L.fk_layernorm_max_cols.argtypes = [i32]
     L.fk_layernorm_max_cols.restype = i64
     L.fk_softmax_onchip_max_cols.argtypes = [i32]
@@ -345,6 +349,25 @@ def fk_linear_gelu(x, w, bias, y, gelu: bool = True, stream=None) -> None:
                                     _dtype_code(x), _stream_handle(x, stream)), "fk_linear_gelu")
 
 
+def fk_attention_fwd(q, k, v, o, causal: bool = True, stream=None) -> None:
+    """o = softmax(q k^T / sqrt(d) + mask) v for 4-D [B, H, T, d] tensors (any strides,
+    contiguous head dimension)."""
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _device_tensor(t, name)
+        if t.dim() != 4 or tuple(t.shape) != tuple(q.shape):
+            raise ValueError(f"fk_attention_fwd: {name} must be 4-D [B, H, T, d] like q")
+        if t.shape[3] > 1 and t.stride(3) != 1:
+            raise ValueError(f"fk_attention_fwd: {name} needs a contiguous head dimension")
+        if t.dtype != q.dtype:
+            raise TypeError("fk_attention_fwd: q, k, v, o must share a dtype")
+    B, H, T, d = q.shape
+    st = (ctypes.c_int64 * 12)(*[int(t.stride(i)) for t in (q, k, v, o) for i in range(3)])
+    with _torch().cuda.device(q.device):
+        _check(lib().fk_attention_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B,
+                                      H, T, d, st, int(bool(causal)), _dtype_code(q),
+                                      _stream_handle(q, stream)), "fk_attention_fwd")
+
+
 def fk_copy(x, y, nbytes: int | None = None, stream=None) -> None:
     """Copy nbytes (default: all of x) from x to y on the device."""
     _device_tensor(x, "x")
@@ -399,3 +422,9 @@ def linear_gelu(x, w, bias=None, gelu: bool = True, stream=None):
     y = _torch().empty((x.shape[0], w.shape[0]), dtype=x.dtype, device=x.device)
     fk_linear_gelu(x, w, bias, y, gelu, stream)
     return y
+
+
+def attention_fwd(q, k, v, causal: bool = True, stream=None):
+    o = _torch().empty(q.shape, dtype=q.dtype, device=q.device)
+    fk_attention_fwd(q, k, v, o, causal, stream)
+    return o

@@ -19,9 +19,10 @@ CSRC = PKG / "csrc"
 INCLUDE = ROOT / "include"
 LIB = PKG / "libfusedops.so"
 SOURCES = ["api.hip", "elementwise.hip", "softmax.hip", "layernorm.hip", "backward.hip",
-           "gemm.hip"]
+           "gemm.hip", "attention.hip"]
 HEADERS = ["device_common.hpp", "ew_kernels.hpp", "softmax_kernels.hpp", "layernorm_kernels.hpp",
-           "backward_kernels.hpp", "gemm_kernels.hpp", "launch.hpp"]
+           "backward_kernels.hpp", "gemm_kernels.hpp", "attention_kernels.hpp",
+           "launch.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

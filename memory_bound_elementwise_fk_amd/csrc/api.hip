@@ -257,6 +257,41 @@ int fk_linear_gelu(const void* x, const void* w, const void* bias, void* y, int6
                                              static_cast<hipStream_t>(stream)));
 }
 
+int fk_attention_fwd(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H,
+                     int64_t T, int64_t d, const int64_t* strides, int causal, int dtype,
+                     void* stream) {
+    if (!dtype_ok(dtype) || B < 0 || H < 0 || T < 0 || d < 1) return FK_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return FK_ERR_INVALID_ARG;
+    if (strides == nullptr) return FK_ERR_INVALID_ARG;
+    if (B == 0 || H == 0 || T == 0) return FK_OK;
+    if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return FK_ERR_INVALID_ARG;
+    for (int i = 0; i < 12; ++i)
+        if (strides[i] < 0) return FK_ERR_INVALID_ARG;
+    for (int t = 0; t < 4; ++t)
+        if (strides[3 * t + 2] < d) return FK_ERR_INVALID_ARG;  // rows of d contiguous values
+    if (dtype != FK_BF16 || d != fk::attention_head_dim()) return FK_ERR_UNSUPPORTED;
+    const uintptr_t addr = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+                           reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o);
+    if ((addr & 15u) != 0) return FK_ERR_UNSUPPORTED;
+    for (int i = 0; i < 12; ++i)
+        if (strides[i] % 8 != 0) return FK_ERR_UNSUPPORTED;
+    if (B * H > 65535 || B > (int64_t(1) << 31) / H) return FK_ERR_UNSUPPORTED;
+    // extent in bytes of each operand: the last element's offset + 1
+    int64_t ext[4];
+    for (int t = 0; t < 4; ++t) {
+        const int64_t* st = strides + 3 * t;
+        if ((B - 1) > kI64Max / 8 / (st[0] + 1) || (H - 1) > kI64Max / 8 / (st[1] + 1) ||
+            (T - 1) > kI64Max / 8 / (st[2] + 1))
+            return FK_ERR_UNSUPPORTED;
+        ext[t] = ((B - 1) * st[0] + (H - 1) * st[1] + (T - 1) * st[2] + d) * 2;
+    }
+    if (ranges_overlap(o, ext[3], q, ext[0]) || ranges_overlap(o, ext[3], k, ext[1]) ||
+        ranges_overlap(o, ext[3], v, ext[2]))
+        return FK_ERR_OVERLAP;
+    return hip_status(fk::launch_attention_fwd(q, k, v, o, B, H, T, strides, causal,
+                                               static_cast<hipStream_t>(stream)));
+}
+
 int64_t fk_layernorm_max_cols(int dtype) {
     if (!dtype_ok(dtype)) return FK_ERR_INVALID_ARG;
     return fk::layernorm_max_cols(static_cast<fk::Dtype>(dtype));

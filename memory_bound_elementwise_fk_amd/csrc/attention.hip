@@ -1,0 +1,36 @@
+// attention.hip -- launcher of the FlashAttention forward kernel
+// (attention_kernels.hpp).
+#include <cmath>
+
+#include "attention_kernels.hpp"
+#include "launch.hpp"
+
+namespace fk {
+
+int64_t attention_head_dim() { return kAttnD; }
+
+hipError_t launch_attention_fwd(const void* q, const void* k, const void* v, void* o, int64_t B,
+                                int64_t H, int64_t T, const int64_t* strides, int causal,
+                                hipStream_t s) {
+    AttnArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.o = static_cast<uint16_t*>(o);
+    a.B = B;
+    a.H = H;
+    a.T = T;
+    a.qb = strides[0]; a.qh = strides[1]; a.qt = strides[2];
+    a.kb = strides[3]; a.kh = strides[4]; a.kt = strides[5];
+    a.vb = strides[6]; a.vh = strides[7]; a.vt = strides[8];
+    a.ob = strides[9]; a.oh = strides[10]; a.ot = strides[11];
+    a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(double(kAttnD)));
+    a.causal = causal;
+    const int64_t nqb = (T + kAttnBQ - 1) / kAttnBQ;
+    void* args[] = {&a};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&attention_fwd_kernel),
+                           dim3(static_cast<unsigned>(nqb), static_cast<unsigned>(B * H)),
+                           dim3(kAttnThreads), args, 0, s);
+}
+
+}  // namespace fk

@@ -67,4 +67,11 @@ hipError_t launch_linear_gelu(const void* x, const void* w, const void* bias, vo
 int64_t linear_tiles(int64_t M, int64_t N);
 int64_t linear_max_tiles();
 
+// FlashAttention forward, bf16, head dimension attention_head_dim();
+// strides[12] = (batch, head, row) strides of q, k, v, o in elements.
+hipError_t launch_attention_fwd(const void* q, const void* k, const void* v, void* o, int64_t B,
+                                int64_t H, int64_t T, const int64_t* strides, int causal,
+                                hipStream_t s);
+int64_t attention_head_dim();
+
 }  // namespace fk

@@ -307,3 +307,40 @@ def linear_abs_bound(x: np.ndarray, w: np.ndarray, rows: np.ndarray | None = Non
     """(|x| |w|^T)_ij in double: the scale of the accumulation error bounds."""
     xd = np.abs(_as_f64(x if rows is None else x[np.asarray(rows)]))
     return xd @ np.abs(_as_f64(w)).T
+
+
+# ------------------------------------------------------------- attention --
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool = True,
+              rows: dict | None = None) -> np.ndarray:
+    """O = softmax(Q K^T / sqrt(d) + mask) V per (batch, head), rounded once.
+
+    q, k, v: [B, H, T, d] (float32, or bf16 as uint16 bits). The causal mask
+    keeps key j for query i when j <= i ("Lecture 6: GPU Kernels and Triton",
+    section 8: the mask q_offset >= kv_offset). Scores and the products use
+    numpy's float64 matmul (a library step); the row softmax is the oracle's
+    own (max, exponentials, sum, normalise, in double); the result is
+    rounded to fp32 and, for bf16 data, then to bf16. ``rows`` maps (b, h)
+    to an array of query indices to compute only those rows (sampling);
+    then the result is {(b, h): [len(rows), d]}.
+    """
+    Bn, Hn, T, d = q.shape
+    scale = 1.0 / np.sqrt(d)
+
+    def one(b, h, qi):
+        qd = _as_f64(q[b, h][qi])
+        kd = _as_f64(k[b, h])
+        vd = _as_f64(v[b, h])
+        sc = (qd @ kd.T) * scale
+        if causal:
+            sc = np.where(np.arange(T)[None, :] <= np.asarray(qi)[:, None], sc, -np.inf)
+        pr = softmax_rows(np.ascontiguousarray(sc))
+        o = (pr @ vd).astype(np.float32)
+        return f32_to_bf16(o).reshape(o.shape) if q.dtype == np.uint16 else o
+
+    if rows is not None:
+        return {key: one(key[0], key[1], np.asarray(idx)) for key, idx in rows.items()}
+    out = np.empty(q.shape, q.dtype)
+    for b in range(Bn):
+        for h in range(Hn):
+            out[b, h] = one(b, h, np.arange(T))
+    return out

@@ -43,7 +43,7 @@ def test_header_declares_the_entry_points():
                  "fk_set_split_wait_limit", "fk_softmax_onchip_max_cols", "fk_copy",
                  "fk_status_string", "fk_layernorm_rows", "fk_layernorm_max_cols",
                  "fk_gelu_tanh_backward", "fk_softmax_rows_backward",
-                 "fk_softmax_backward_max_cols", "fk_linear_gelu"):
+                 "fk_softmax_backward_max_cols", "fk_linear_gelu", "fk_attention_fwd"):
         assert want in names
 
 
@@ -231,6 +231,32 @@ def test_linear_validation(L):
     assert f(A + 2, B, None, Y, 4, 10, 16, 16, 16, 10, 1, bf, None) == fk.FK_ERR_UNSUPPORTED
     assert f(A, B, None, A + 32, 4, 10, 16, 16, 16, 10, 1, bf, None) == fk.FK_ERR_OVERLAP
     assert f(A, B, Y + 4, Y, 4, 10, 16, 16, 16, 10, 1, bf, None) == fk.FK_ERR_OVERLAP
+
+
+def test_attention_validation(L):
+    import ctypes
+    f = L.fk_attention_fwd
+    C, D = 0x7F0000C00000, 0x7F0000E00000
+    bf = fk.FK_BF16
+
+    def st(*vals):
+        return (ctypes.c_int64 * 12)(*vals)
+
+    good = st(*([2 * 3 * 128, 3 * 128, 128] * 4))      # [B=2, H=... ] contiguous, d = 128
+    assert f(A, B, C, D, 0, 3, 16, 128, good, 1, bf, None) == fk.FK_OK
+    assert f(A, B, C, D, 2, 3, 16, 128, None, 1, bf, None) == fk.FK_ERR_INVALID_ARG
+    assert f(A, B, C, D, -1, 3, 16, 128, good, 1, bf, None) == fk.FK_ERR_INVALID_ARG
+    assert f(A, B, C, D, 2, 3, 16, 128, good, 2, bf, None) == fk.FK_ERR_INVALID_ARG
+    assert f(None, B, C, D, 2, 3, 16, 128, good, 1, bf, None) == fk.FK_ERR_INVALID_ARG
+    assert f(A, B, C, D, 2, 3, 16, 64, good, 1, bf, None) == fk.FK_ERR_UNSUPPORTED   # d != 128
+    assert f(A, B, C, D, 2, 3, 16, 128, good, 1, fk.FK_F32, None) == fk.FK_ERR_UNSUPPORTED
+    assert f(A + 8, B, C, D, 2, 3, 16, 128, good, 1, bf, None) == fk.FK_ERR_UNSUPPORTED
+    short = st(*([2 * 3 * 128, 3 * 128, 100] * 4))     # row stride < d
+    assert f(A, B, C, D, 2, 3, 16, 128, short, 1, bf, None) == fk.FK_ERR_INVALID_ARG
+    odd = st(*([2 * 3 * 136, 3 * 136, 132] * 4))       # stride not a multiple of 8
+    assert f(A, B, C, D, 2, 3, 16, 128, odd, 1, bf, None) == fk.FK_ERR_UNSUPPORTED
+    assert f(A, B, C, A + 256, 2, 3, 16, 128, good, 1, bf, None) == fk.FK_ERR_OVERLAP
+    assert f(A, B, C, D, 300, 300, 16, 128, good, 1, bf, None) == fk.FK_ERR_UNSUPPORTED  # B*H
 
 
 def test_copy_validation(L):

@@ -1,0 +1,118 @@
+"""GPU parity of the FlashAttention forward kernel against the CPU oracle.
+Needs an MI355X.
+
+Tolerance (derived from the kernel's arithmetic; the pages and the north
+star fix none for attention): |o - r| <= ulp_bf16(|r|) + 2^-8 max|v| per
+(batch, head). O = sum_j p_j v_j / l. The kernel rounds p_j to bf16 before
+the P V product (as the page's kernel rounds P to V's dtype): relative error
+<= 2^-9 per weight, so at most 2^-9 max|v| after the division by l (the sum
+l uses the unrounded p); the fp32 scores (128 bf16 products) move the
+weights by ~1e-4 relative, far below that; the output rounding to bf16 adds
+half an ulp on each side. 2^-8 leaves a factor 2 over the P rounding.
+"""
+import numpy as np
+import pytest
+import torch
+
+import memory_bound_elementwise_fk_amd as fk
+import oracle
+from memory_bound_elementwise_fk_amd import workloads as wl
+from tests.gpu_util import DEV, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def bf16_ulp(r):
+    e = np.floor(np.log2(np.maximum(np.abs(r), 2.0 ** -126)))
+    return np.exp2(e - 7)
+
+
+def qkv(B, H, T, seed, d=128):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(3):
+        a = rng.standard_normal((B, H, T, d)).astype(np.float32)
+        out.append(wl.f32_to_bf16_bits(a).reshape(B, H, T, d))
+    return out
+
+
+def check_rows(got_rows, ref_rows, v, what):
+    """got_rows / ref_rows: {(b, h): [n, d] bf16}."""
+    for key, ref in ref_rows.items():
+        g = oracle.bf16_to_f32(got_rows[key]).astype(np.float64)
+        r = oracle.bf16_to_f32(ref).astype(np.float64)
+        vmax = float(np.abs(oracle.bf16_to_f32(v[key[0], key[1]])).max())
+        lim = bf16_ulp(r) + 2.0 ** -8 * vmax
+        err = np.abs(g - r)
+        bad = np.flatnonzero(err > lim)
+        assert bad.size == 0, f"{what} {key}: {bad.size} beyond tolerance, worst excess {(err - lim).max():.3e}"
+
+
+def run(q, k, v, causal):
+    o = fk.attention_fwd(to_dev(q), to_dev(k), to_dev(v), causal=causal)
+    return to_host(o)
+
+
+@pytest.mark.parametrize("B,H,T", [(1, 1, 1), (1, 2, 33), (2, 3, 128), (1, 2, 200), (1, 1, 513),
+                                   (2, 2, 1000)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_attention_shapes(B, H, T, causal):
+    q, k, v = qkv(B, H, T, seed=B * 100 + H * 10 + T)
+    got = run(q, k, v, causal)
+    ref = oracle.attention(q, k, v, causal=causal)
+    rows = {(b, h): np.arange(T) for b in range(B) for h in range(H)}
+    check_rows({key: got[key[0], key[1]] for key in rows},
+               {key: ref[key[0], key[1]] for key in rows}, v, f"B{B} H{H} T{T} causal={causal}")
+
+
+def test_attention_strided_bthd_layout():
+    # tensors stored as [B, T, H, d] and viewed as [B, H, T, d]
+    B, H, T, d = 2, 4, 300, 128
+    rng = np.random.default_rng(7)
+    base = [wl.f32_to_bf16_bits(rng.standard_normal((B, T, H, d)).astype(np.float32))
+            .reshape(B, T, H, d) for _ in range(3)]
+    qt, kt, vt = (to_dev(a).permute(0, 2, 1, 3) for a in base)
+    ot = torch.empty((B, T, H, d), dtype=torch.bfloat16, device=DEV).permute(0, 2, 1, 3)
+    fk.fk_attention_fwd(qt, kt, vt, ot, causal=True)
+    got = to_host(ot.contiguous())
+    q, k, v = (np.ascontiguousarray(a.transpose(0, 2, 1, 3)) for a in base)
+    ref = oracle.attention(q, k, v, causal=True)
+    rows = {(b, h): np.arange(T) for b in range(B) for h in range(H)}
+    check_rows({key: got[key[0], key[1]] for key in rows},
+               {key: ref[key[0], key[1]] for key in rows}, v, "B,T,H,d layout")
+
+
+@pytest.mark.parametrize("T", [128, 1024, 4096])
+def test_attention_benchmark_grid_sampled(T):
+    # the pages' benchmark grid: B = 4, H = 32, d = 128
+    B, H = 4, 32
+    q, k, v = qkv(B, H, T, seed=T)
+    for causal in (True, False):
+        o = fk.attention_fwd(to_dev(q), to_dev(k), to_dev(v), causal=causal)
+        rng = np.random.default_rng(T + causal)
+        picks = {(int(b), int(h)): np.sort(rng.choice(T, min(T, 24), replace=False))
+                 for b, h in zip(rng.integers(0, B, 4), rng.integers(0, H, 4))}
+        ref = oracle.attention(q, k, v, causal=causal, rows=picks)
+        got = {key: to_host(o[key[0], key[1]][torch.from_numpy(idx).to(DEV)])
+               for key, idx in picks.items()}
+        check_rows(got, ref, v, f"T={T} causal={causal}")
+
+
+def test_attention_closed_forms():
+    # Q = 0: uniform weights, the causal output is the prefix mean of V
+    B, H, T = 1, 1, 300
+    q = np.zeros((B, H, T, 128), np.uint16)
+    _, k, v = qkv(B, H, T, seed=3)
+    got = oracle.bf16_to_f32(run(q, k, v, True)[0, 0]).astype(np.float64)
+    vf = oracle.bf16_to_f32(v[0, 0]).astype(np.float64)
+    prefix = np.cumsum(vf, axis=0) / np.arange(1, T + 1)[:, None]
+    assert np.abs(got - prefix).max() <= bf16_ulp(prefix).max() + 2.0 ** -8 * np.abs(vf).max()
+    # row 0 under the causal mask is V[0] exactly (one weight of 1)
+    assert np.array_equal(run(*qkv(1, 2, 77, seed=4), True)[:, :, 0], qkv(1, 2, 77, seed=4)[2][:, :, 0])
+
+
+def test_attention_bitwise_reproducible():
+    q, k, v = (to_dev(a) for a in qkv(2, 4, 700, seed=5))
+    a = fk.attention_fwd(q, k, v)
+    b = fk.attention_fwd(q, k, v)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
