@@ -395,6 +395,25 @@ def measure_extras(fk, wl, torch, xs, ys, stream):
         "library_linear_then_gelu_ms": round(lib_unfused, 4),
         "note": "library = torch.nn.functional.linear (hipBLASLt) and its separate GELU"}
     del xl, wlin, bl, yl
+
+    # FlashAttention forward on the pages' benchmark grid (B = 4, H = 32,
+    # d = 128), against torch's scaled_dot_product_attention
+    att = {}
+    for T in (1024, 4096):
+        qa, ka, va = (wl_.to_torch(wl_.draw(4 * 32 * T * 128, seed=6 + i, dtype="bf16"),
+                                   "cuda:0").view(4, 32, T, 128) for i in range(3))
+        oa = torch.empty_like(qa)
+        for causal in (False, True):
+            fl = 4.0 * 4 * 32 * T * T * 128 * (0.5 if causal else 1.0)
+            ms_fk = avg_ms(lambda: fk.fk_attention_fwd(qa, ka, va, oa, causal=causal), 5)
+            ms_lib = avg_ms(lambda: torch.nn.functional.scaled_dot_product_attention(
+                qa, ka, va, is_causal=causal), 5)
+            att[f"T{T}_{'causal' if causal else 'full'}"] = {
+                "ms": round(ms_fk, 4), "TFLOPs": round(fl / (ms_fk * 1e-3) / 1e12, 1),
+                "frac_of_mfma_peak": round(fl / (ms_fk * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "library_sdpa_ms": round(ms_lib, 4)}
+        del qa, ka, va, oa
+    out["attention_fwd"] = att
     out["chain_fused_vs_unfused"] = {
         "fused_ms": round(fused_ms, 5), "unfused_ms": round(unfused_ms, 5),
         "fused_bytes": fb, "unfused_bytes": ub,

@@ -96,18 +96,34 @@ __global__ __launch_bounds__(kAttnThreads) void attention_fwd_kernel(AttnArgs a)
     const int64_t kend = a.causal ? q_last : a.T;
     const int64_t nkb = (kend + kAttnBC - 1) / kAttnBC;
 
-    // staging: thread tid moves chunks c = tid + i * threads (key c / 16,
-    // dims (c % 16) * 8 .. + 8) of K and V
-    u32x4 rk[kAttnLoads], rv[kAttnLoads];
+    // Staging. K: thread tid moves chunks c = tid + i * threads (key c / 16,
+    // dims (c % 16) * 8 .. + 8), stored row-major. V is stored transposed
+    // (V^T[dim][key]); thread tid takes the key pair 2 p, 2 p + 1
+    // (p = tid % 32) and dims 8 (tid / 32 + 8 i) .. + 8, and writes each dim
+    // of the pair as one 32-bit word: the 64 lanes of a wave then write 32
+    // consecutive words of one V^T row and 32 of the row 8 dims further
+    // (1152 bytes apart, the other half of the banks), without conflicts.
+    constexpr int kVPairs = kAttnBC / 2;                            // 32 key pairs
+    constexpr int kVRounds = (kAttnD / 8) / (kAttnThreads / kVPairs);  // dim blocks per thread
+    u32x4 rk[kAttnLoads], rv[2 * kVRounds];
     auto load_block = [&](int64_t kb0) {
 #pragma unroll
         for (int i = 0; i < kAttnLoads; ++i) {
             const int c = tid + i * kAttnThreads;
             const int64_t key = kb0 + c / (kAttnD / 8);
             const int dim = (c % (kAttnD / 8)) * 8;
-            const bool ok = key < a.T;
-            rk[i] = ok ? *reinterpret_cast<const u32x4*>(Kg + key * a.kt + dim) : u32x4{0u, 0u, 0u, 0u};
-            rv[i] = ok ? *reinterpret_cast<const u32x4*>(Vg + key * a.vt + dim) : u32x4{0u, 0u, 0u, 0u};
+            rk[i] = key < a.T ? *reinterpret_cast<const u32x4*>(Kg + key * a.kt + dim)
+                              : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int i = 0; i < kVRounds; ++i) {
+            const int64_t key = kb0 + 2 * (tid % kVPairs);
+            const int dim = 8 * (tid / kVPairs + i * (kAttnThreads / kVPairs));
+            rv[2 * i] = key < a.T ? *reinterpret_cast<const u32x4*>(Vg + key * a.vt + dim)
+                                  : u32x4{0u, 0u, 0u, 0u};
+            rv[2 * i + 1] = key + 1 < a.T
+                                ? *reinterpret_cast<const u32x4*>(Vg + (key + 1) * a.vt + dim)
+                                : u32x4{0u, 0u, 0u, 0u};
         }
     };
     auto store_block = [&](int buf) {
@@ -117,11 +133,21 @@ __global__ __launch_bounds__(kAttnThreads) void attention_fwd_kernel(AttnArgs a)
             const int key = c / (kAttnD / 8);
             const int dim = (c % (kAttnD / 8)) * 8;
             *reinterpret_cast<u32x4*>(&Ks[buf][key * kKStride + dim]) = rk[i];
-            const uint32_t w[4] = {rv[i].x, rv[i].y, rv[i].z, rv[i].w};
+        }
+#pragma unroll
+        for (int i = 0; i < kVRounds; ++i) {
+            const int key = 2 * (tid % kVPairs);
+            const int dim = 8 * (tid / kVPairs + i * (kAttnThreads / kVPairs));
+            const uint32_t a0[4] = {rv[2 * i].x, rv[2 * i].y, rv[2 * i].z, rv[2 * i].w};
+            const uint32_t a1[4] = {rv[2 * i + 1].x, rv[2 * i + 1].y, rv[2 * i + 1].z,
+                                    rv[2 * i + 1].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                Vt[buf][(dim + 2 * e) * kVtStride + key] = static_cast<uint16_t>(w[e] & 0xFFFFu);
-                Vt[buf][(dim + 2 * e + 1) * kVtStride + key] = static_cast<uint16_t>(w[e] >> 16);
+                // dims dim + 2e (low halves) and dim + 2e + 1 (high halves)
+                *reinterpret_cast<uint32_t*>(&Vt[buf][(dim + 2 * e) * kVtStride + key]) =
+                    (a0[e] & 0xFFFFu) | (a1[e] << 16);
+                *reinterpret_cast<uint32_t*>(&Vt[buf][(dim + 2 * e + 1) * kVtStride + key]) =
+                    (a0[e] >> 16) | (a1[e] & 0xFFFF0000u);
             }
         }
     };
