@@ -16,12 +16,15 @@ hipError_t launch_kernel(const void* fn, int64_t grid, int block, hipStream_t s,
 }
 
 // Row shapes (waves per row, 16-byte vectors per lane), smallest first; the
-// first that covers the row is used (the softmax's table: at most 4 vectors
-// per lane until the widest shape).
+// first that covers the row is used. At most 2 vectors per lane until the
+// widest shapes: the LayerNorm epilogue (gamma, beta, GELU) needs more
+// registers per value than the softmax, and with 4 vectors per lane a bf16
+// 4096-column row held the waves to 2 per SIMD (184 VGPRs), too few
+// bytes in flight for HBM.
 struct LnShape {
     int wpr, vpl;
 };
-constexpr LnShape kLnShapes[] = {{1, 1}, {1, 2}, {1, 4}, {2, 4}, {4, 4}, {8, 4}, {16, 4}, {16, 8}};
+constexpr LnShape kLnShapes[] = {{1, 1}, {1, 2}, {2, 2}, {4, 2}, {8, 2}, {16, 2}, {16, 4}, {16, 8}};
 constexpr int kNumLnShapes = sizeof(kLnShapes) / sizeof(kLnShapes[0]);
 constexpr bool kLnNT = true;  // x read once, y written once
 
@@ -38,9 +41,11 @@ hipError_t launch_ln(const void* x, void* y, int64_t rows, int64_t cols, int64_t
     int64_t grid = (rows + kRowsPerWg - 1) / kRowsPerWg;
     if (grid > kMaxWorkItems / kThreads) grid = kMaxWorkItems / kThreads;
     const void* fn =
-        vec ? reinterpret_cast<const void*>(&layernorm_reg_kernel<IO, WPR, VPL, true, kLnNT>)
-            : reinterpret_cast<const void*>(&layernorm_reg_kernel<IO, WPR, VPL, false>);
-    return launch_kernel(fn, grid, kThreads, s, x, y, rows, cols, ldx, ldy, g, b, eps, gelu);
+        vec ? (gelu ? reinterpret_cast<const void*>(&layernorm_reg_kernel<IO, WPR, VPL, true, true, kLnNT>)
+                    : reinterpret_cast<const void*>(&layernorm_reg_kernel<IO, WPR, VPL, true, false, kLnNT>))
+            : (gelu ? reinterpret_cast<const void*>(&layernorm_reg_kernel<IO, WPR, VPL, false, true>)
+                    : reinterpret_cast<const void*>(&layernorm_reg_kernel<IO, WPR, VPL, false, false>));
+    return launch_kernel(fn, grid, kThreads, s, x, y, rows, cols, ldx, ldy, g, b, eps);
 }
 
 template <class IO>
@@ -56,10 +61,10 @@ hipError_t launch_ln_t(const void* x, void* y, int64_t rows, int64_t cols, int64
     switch (shape) {
         case 0: return launch_ln<IO, 1, 1>(x, y, rows, cols, ldx, ldy, g, b, eps, gelu, vec, s);
         case 1: return launch_ln<IO, 1, 2>(x, y, rows, cols, ldx, ldy, g, b, eps, gelu, vec, s);
-        case 2: return launch_ln<IO, 1, 4>(x, y, rows, cols, ldx, ldy, g, b, eps, gelu, vec, s);
-        case 3: return launch_ln<IO, 2, 4>(x, y, rows, cols, ldx, ldy, g, b, eps, gelu, vec, s);
-        case 4: return launch_ln<IO, 4, 4>(x, y, rows, cols, ldx, ldy, g, b, eps, gelu, vec, s);
-        case 5: return launch_ln<IO, 8, 4>(x, y, rows, cols, ldx, ldy, g, b, eps, gelu, vec, s);
+        case 2: return launch_ln<IO, 2, 2>(x, y, rows, cols, ldx, ldy, g, b, eps, gelu, vec, s);
+        case 3: return launch_ln<IO, 4, 2>(x, y, rows, cols, ldx, ldy, g, b, eps, gelu, vec, s);
+        case 4: return launch_ln<IO, 8, 2>(x, y, rows, cols, ldx, ldy, g, b, eps, gelu, vec, s);
+        case 5: return launch_ln<IO, 16, 2>(x, y, rows, cols, ldx, ldy, g, b, eps, gelu, vec, s);
         case 6: return launch_ln<IO, 16, 4>(x, y, rows, cols, ldx, ldy, g, b, eps, gelu, vec, s);
         default: return launch_ln<IO, 16, 8>(x, y, rows, cols, ldx, ldy, g, b, eps, gelu, vec, s);
     }

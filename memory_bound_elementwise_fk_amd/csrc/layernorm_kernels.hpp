@@ -22,49 +22,10 @@
 
 namespace fk {
 
-// Multiply by gamma and add beta, column by column, in load_span's layout.
-// gamma / beta are per-column arrays of the row dtype, or null (1 / 0).
-template <class IO, int VPL, int LANES, bool VEC>
-__device__ inline void affine_span(const char* gp, const char* bp, int64_t cols, int lane,
-                                   float (&v)[VPL * IO::kVec]) {
-    constexpr int V = IO::kVec;
-    if constexpr (VEC) {
-#pragma unroll
-        for (int k = 0; k < VPL; ++k) {
-            const int64_t c = (int64_t(k) * LANES + lane) * V;
-            float g[V] = {}, b[V] = {};
-            if (c + V <= cols) {
-                if (gp) IO::unpack(ld16<false>(reinterpret_cast<const u32x4*>(gp + c * IO::kBytes)), g);
-                if (bp) IO::unpack(ld16<false>(reinterpret_cast<const u32x4*>(bp + c * IO::kBytes)), b);
-            } else {
-#pragma unroll
-                for (int e = 0; e < V; ++e) {
-                    g[e] = (gp && c + e < cols) ? IO::load1(gp, c + e) : 1.0f;
-                    b[e] = (bp && c + e < cols) ? IO::load1(bp, c + e) : 0.0f;
-                }
-            }
-#pragma unroll
-            for (int e = 0; e < V; ++e) {
-                if (gp) v[k * V + e] *= g[e];
-                if (bp) v[k * V + e] += b[e];
-            }
-        }
-    } else {
-#pragma unroll
-        for (int k = 0; k < VPL * V; ++k) {
-            const int64_t c = int64_t(k) * LANES + lane;
-            if (c < cols) {
-                if (gp) v[k] *= IO::load1(gp, c);
-                if (bp) v[k] += IO::load1(bp, c);
-            }
-        }
-    }
-}
-
-template <class IO, int WPR, int VPL, bool VEC, bool NT = false>
+template <class IO, int WPR, int VPL, bool VEC, bool GELU, bool NT = false>
 __global__ __launch_bounds__(reg_threads<WPR>()) void layernorm_reg_kernel(
     const void* x, void* y, int64_t rows, int64_t cols, int64_t ldx, int64_t ldy,
-    const void* gamma, const void* beta, float eps, int gelu) {
+    const void* gamma, const void* beta, float eps) {
     constexpr int V = IO::kVec;
     constexpr int E = VPL * V;
     constexpr int kRowLanes = WPR * kWave;
@@ -107,15 +68,29 @@ __global__ __launch_bounds__(reg_threads<WPR>()) void layernorm_reg_kernel(
         }
         const float mu = s / n;
 
-        // deviations, their sum (the correction) and their squares
+        // deviations, their sum (the correction) and their squares; columns
+        // past the row end (only in a ragged row) contribute 0
         float a = 0.0f, q = 0.0f;
+        if (full) {
 #pragma unroll
-        for (int i = 0; i < E; ++i) {
-            float d = v[i] - mu;
-            if (!full && span_col<IO, kRowLanes, VEC>(i, lr) >= cols) d = 0.0f;
-            v[i] = d;
-            a += d;
-            q = fmaf(d, d, q);
+            for (int i = 0; i < E; ++i) {
+                const float d = v[i] - mu;
+                v[i] = d;
+                a += d;
+                q = fmaf(d, d, q);
+            }
+        } else {
+            const int ncols = static_cast<int>(cols);
+#pragma unroll
+            for (int i = 0; i < E; ++i) {
+                // column of value i: vector layout (i / V * lanes + lane) * V + i % V,
+                // scalar layout i * lanes + lane
+                const int col = VEC ? ((i / V) * kRowLanes + lr) * V + i % V : i * kRowLanes + lr;
+                const float d = col < ncols ? v[i] - mu : 0.0f;
+                v[i] = d;
+                a += d;
+                q = fmaf(d, d, q);
+            }
         }
         a = wave_sum(a);
         q = wave_sum(q);
@@ -138,13 +113,56 @@ __global__ __launch_bounds__(reg_threads<WPR>()) void layernorm_reg_kernel(
         const float var = fmaxf(q / n - c * c, 0.0f);
         const float rstd = 1.0f / sqrtf(var + eps);
 
-        // normalise, affine, optional GELU, write back
+        // normalise, gamma and beta, optional GELU, write back -- one
+        // 16-byte vector (or, on the scalar layout, eight values) at a time,
+        // which keeps the epilogue's temporaries to one vector of registers
+        char* yr = row_ptr<IO>(y, row, ldy);
+        constexpr int kChunk = VEC ? V : (E < 8 ? E : 8);  // divides E (E = VPL * V)
+        static_assert(E % kChunk == 0, "chunks cover the lane's values");
+        // columns of value e of chunk k: c0 + e (vector layout: one 16-byte
+        // vector) or c0 + e * kRowLanes (scalar layout); rows held on chip
+        // are at most 65536 columns, so 32-bit column indices suffice
+        constexpr int kStep = VEC ? 1 : kRowLanes;
+        const int ncols = static_cast<int>(cols);
 #pragma unroll
-        for (int i = 0; i < E; ++i) v[i] = (v[i] - c) * rstd;
-        if (gp || bp) affine_span<IO, VPL, kRowLanes, VEC>(gp, bp, cols, lr, v);
-        if (gelu) gelu_tanh_n(v);
-        if (active)
-            store_span<IO, VPL, kRowLanes, VEC, NT>(row_ptr<IO>(y, row, ldy), cols, 0, lr, v);
+        for (int k = 0; k < E / kChunk; ++k) {
+            const int c0 = VEC ? (k * kRowLanes + lr) * V : k * kChunk * kRowLanes + lr;
+            float t[kChunk], gv[kChunk], bv[kChunk];
+#pragma unroll
+            for (int e = 0; e < kChunk; ++e) {
+                t[e] = (v[k * kChunk + e] - c) * rstd;
+                gv[e] = 1.0f;
+                bv[e] = 0.0f;
+            }
+            const bool whole = VEC && c0 + kChunk <= ncols;  // an unmasked 16-byte vector
+            if (whole) {
+                if (gp) IO::unpack(ld16<false>(reinterpret_cast<const u32x4*>(gp + int64_t(c0) * IO::kBytes)), gv);
+                if (bp) IO::unpack(ld16<false>(reinterpret_cast<const u32x4*>(bp + int64_t(c0) * IO::kBytes)), bv);
+            } else {
+#pragma unroll
+                for (int e = 0; e < kChunk; ++e) {
+                    const int col = c0 + e * kStep;
+                    if (gp && col < ncols) gv[e] = IO::load1(gp, col);
+                    if (bp && col < ncols) bv[e] = IO::load1(bp, col);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < kChunk; ++e) {
+                if (gp) t[e] *= gv[e];
+                if (bp) t[e] += bv[e];
+            }
+            if constexpr (GELU) gelu_tanh_n(t);
+            if (!active) continue;
+            if (whole) {
+                st16<NT>(reinterpret_cast<u32x4*>(yr + int64_t(c0) * IO::kBytes), IO::pack(t));
+            } else {
+#pragma unroll
+                for (int e = 0; e < kChunk; ++e) {
+                    const int col = c0 + e * kStep;
+                    if (col < ncols) IO::store1(yr, col, t[e]);
+                }
+            }
+        }
     }
 }
 
