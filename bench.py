@@ -328,23 +328,31 @@ def measure_extras(fk, wl, torch, xs, ys, stream):
     # the C2 row shape (fp32 4096 x 1000, rows shifted every 16th); the
     # algorithmic bytes are one read of x and one write of y (gamma and beta,
     # 2 * cols elements, are counted once)
+    import numpy as np
+
     from memory_bound_elementwise_fk_amd import workloads as wl_
 
     ln = {}
-    xb = xs["C4"]
-    gb = torch.ones(xb.shape[1], dtype=xb.dtype, device=xb.device)
-    bb = torch.zeros_like(gb)
+    # x ~ 8 N(0, 1) (C4's shape and scale, without its masked entries),
+    # gamma ~ 1 + 0.25 N(0, 1), beta ~ 0.5 N(0, 1)
+    xb = wl_.to_torch(wl_.draw(32768 * 4096, seed=0, scale=8.0, dtype="bf16"),
+                      "cuda:0").view(32768, 4096)
+    prng = np.random.default_rng(8)
+    gb = wl_.to_torch(wl_.f32_to_bf16_bits(
+        (1.0 + 0.25 * prng.standard_normal(4096)).astype(np.float32)), "cuda:0")
+    bb = wl_.to_torch(wl_.f32_to_bf16_bits(
+        (0.5 * prng.standard_normal(4096)).astype(np.float32)), "cuda:0")
     yb = torch.empty_like(xb)
     ms = avg_ms(lambda: fk.fk_layernorm_rows(xb, yb, gb, bb, gelu=True), 20)
     nb = 2 * xb.numel() * 2 + 2 * xb.shape[1] * 2
     ln["bf16_32768x4096_gelu"] = {"ms": round(ms, 5), "bytes": nb,
                                   "GBps": round(nb / (ms * 1e-3) / 1e9, 1),
                                   "frac_of_peak": round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-    del yb
+    del xb, yb
     xf = wl_.to_torch(wl_.make_input("C2"), "cuda:0")
     yf = torch.empty_like(xf)
-    gf = torch.ones(xf.shape[1], dtype=xf.dtype, device=xf.device)
-    bf = torch.zeros_like(gf)
+    gf = torch.from_numpy((1.0 + 0.25 * prng.standard_normal(1000)).astype(np.float32)).to("cuda:0")
+    bf = torch.from_numpy((0.5 * prng.standard_normal(1000)).astype(np.float32)).to("cuda:0")
     ms = avg_ms(lambda: fk.fk_layernorm_rows(xf, yf, gf, bf), 50)
     nb = 2 * xf.numel() * 4 + 2 * xf.shape[1] * 4
     ln["f32_4096x1000"] = {"ms": round(ms, 5), "bytes": nb,

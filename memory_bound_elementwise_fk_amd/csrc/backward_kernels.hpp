@@ -106,9 +106,9 @@ __global__ __launch_bounds__(reg_threads<WPR>()) void softmax_bwd_reg_kernel(
         const bool active = row < rows;
         float vy[E], vg[E];
         if (active) {
-            load_span<IO, VPL, kRowLanes, VEC, NT>(row_ptr<IO>(y, row, ldy), cols, 0, lr, vy, 0.0f);
-            load_span<IO, VPL, kRowLanes, VEC, NT>(row_ptr<IO>(dy, row, lddy), cols, 0, lr, vg,
-                                                   0.0f);
+            load_span2<IO, VPL, kRowLanes, VEC, NT>(row_ptr<IO>(y, row, ldy),
+                                                    row_ptr<IO>(dy, row, lddy), cols, 0, lr, vy,
+                                                    vg, 0.0f);
         } else {
 #pragma unroll
             for (int i = 0; i < E; ++i) vy[i] = vg[i] = 0.0f;

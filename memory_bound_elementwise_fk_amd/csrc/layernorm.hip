@@ -17,10 +17,9 @@ hipError_t launch_kernel(const void* fn, int64_t grid, int block, hipStream_t s,
 
 // Row shapes (waves per row, 16-byte vectors per lane), smallest first; the
 // first that covers the row is used. At most 2 vectors per lane until the
-// widest shapes: the LayerNorm epilogue (gamma, beta, GELU) needs more
-// registers per value than the softmax, and with 4 vectors per lane a bf16
-// 4096-column row held the waves to 2 per SIMD (184 VGPRs), too few
-// bytes in flight for HBM.
+// widest shapes: a lane also holds gamma and beta of its columns, so the
+// LayerNorm needs about three registers per value where the softmax needs
+// one (bf16 4096 columns: 4 waves x 2 vectors, 83 VGPRs, 5 waves per SIMD).
 struct LnShape {
     int wpr, vpl;
 };
@@ -40,11 +39,15 @@ hipError_t launch_ln(const void* x, void* y, int64_t rows, int64_t cols, int64_t
     constexpr int kRowsPerWg = kThreads / (WPR * kWave);
     int64_t grid = (rows + kRowsPerWg - 1) / kRowsPerWg;
     if (grid > kMaxWorkItems / kThreads) grid = kMaxWorkItems / kThreads;
+    // a row that fills the shape exactly runs the variant without masks
+    const bool full = vec && cols == ln_capacity<IO>(LnShape{WPR, VPL});
     const void* fn =
-        vec ? (gelu ? reinterpret_cast<const void*>(&layernorm_reg_kernel<IO, WPR, VPL, true, true, kLnNT>)
-                    : reinterpret_cast<const void*>(&layernorm_reg_kernel<IO, WPR, VPL, true, false, kLnNT>))
-            : (gelu ? reinterpret_cast<const void*>(&layernorm_reg_kernel<IO, WPR, VPL, false, true>)
-                    : reinterpret_cast<const void*>(&layernorm_reg_kernel<IO, WPR, VPL, false, false>));
+        full ? (gelu ? reinterpret_cast<const void*>(&layernorm_reg_kernel<IO, WPR, VPL, true, true, kLnNT, true>)
+                     : reinterpret_cast<const void*>(&layernorm_reg_kernel<IO, WPR, VPL, true, false, kLnNT, true>))
+        : vec ? (gelu ? reinterpret_cast<const void*>(&layernorm_reg_kernel<IO, WPR, VPL, true, true, kLnNT>)
+                      : reinterpret_cast<const void*>(&layernorm_reg_kernel<IO, WPR, VPL, true, false, kLnNT>))
+              : (gelu ? reinterpret_cast<const void*>(&layernorm_reg_kernel<IO, WPR, VPL, false, true>)
+                      : reinterpret_cast<const void*>(&layernorm_reg_kernel<IO, WPR, VPL, false, false>));
     return launch_kernel(fn, grid, kThreads, s, x, y, rows, cols, ldx, ldy, g, b, eps);
 }
 

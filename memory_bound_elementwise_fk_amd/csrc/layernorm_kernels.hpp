@@ -12,17 +12,56 @@
 // softmax), so HBM is read once and written once. Statistics use the
 // corrected two-pass scheme over registers: mu = sum(x) / n, then
 // d = x - mu, a = sum(d), q = sum(d^2), c = a / n, var = q / n - c^2 and the
-// output uses (d - c); the correction c removes the rounding of mu, so the
-// error does not grow with |mu| (rows shifted far from 0). Reductions are
-// lane-local, DPP across the wave, LDS across the row's waves, in a fixed
-// order (bitwise reproducible).
+// output is (d - c) rstd, formed as fma(d, rstd, -c rstd); the correction c
+// removes the rounding of mu, so the error does not grow with |mu| (rows
+// shifted far from 0). Reductions are lane-local, DPP across the wave, LDS
+// across the row's waves, in a fixed order (bitwise reproducible). gamma
+// and beta are loaded before the row's statistics (not after them, where
+// their latency would add to every row's) and applied with one more fma.
 #pragma once
 
 #include "softmax_kernels.hpp"
 
 namespace fk {
 
-template <class IO, int WPR, int VPL, bool VEC, bool GELU, bool NT = false>
+// gamma and beta of value chunk k of a lane (values k*V .. k*V+V-1 in
+// load_span's layout; 1 and 0 where absent or past the row end).
+template <class IO, int LANES, bool VEC>
+__device__ inline void affine_chunk(const char* gp, const char* bp, int64_t cols, int lane, int k,
+                                    float (&g)[IO::kVec], float (&b)[IO::kVec]) {
+    constexpr int V = IO::kVec;
+    if constexpr (VEC) {
+        const int64_t c0 = (int64_t(k) * LANES + lane) * V;
+        if (c0 + V <= cols) {
+            if (gp) IO::unpack(ld16<false>(reinterpret_cast<const u32x4*>(gp + c0 * IO::kBytes)), g);
+            else
+#pragma unroll
+                for (int e = 0; e < V; ++e) g[e] = 1.0f;
+            if (bp) IO::unpack(ld16<false>(reinterpret_cast<const u32x4*>(bp + c0 * IO::kBytes)), b);
+            else
+#pragma unroll
+                for (int e = 0; e < V; ++e) b[e] = 0.0f;
+            return;
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+        const int64_t col = span_col<IO, LANES, VEC>(k * V + e, lane);
+        g[e] = (gp && col < cols) ? IO::load1(gp, col) : 1.0f;
+        b[e] = (bp && col < cols) ? IO::load1(bp, col) : 0.0f;
+    }
+}
+
+// gamma and beta are held in registers (loaded once per workgroup, before
+// the first row, so their latency overlaps the row loads) up to this many
+// vectors per lane; wider shapes load them vector by vector in the
+// epilogue, which keeps the register count of the widest rows bounded.
+constexpr int kLnHoldAffineVpl = 2;
+
+// FULL: the launcher guarantees cols == WPR * 64 * VPL * V (the row fills
+// the shape exactly, on the vector layout), so no masking code is compiled;
+// ragged rows take FULL = false.
+template <class IO, int WPR, int VPL, bool VEC, bool GELU, bool NT = false, bool FULL = false>
 __global__ __launch_bounds__(reg_threads<WPR>()) void layernorm_reg_kernel(
     const void* x, void* y, int64_t rows, int64_t cols, int64_t ldx, int64_t ldy,
     const void* gamma, const void* beta, float eps) {
@@ -30,24 +69,53 @@ __global__ __launch_bounds__(reg_threads<WPR>()) void layernorm_reg_kernel(
     constexpr int E = VPL * V;
     constexpr int kRowLanes = WPR * kWave;
     constexpr int kRowsPerWg = reg_threads<WPR>() / kRowLanes;
-    __shared__ float red[2][kRowsPerWg * WPR];
+    constexpr bool kHold = VPL <= kLnHoldAffineVpl;
+    // partial sums of the row's waves: [parity][sum x, sum d, sum d^2][row, wave].
+    // Consecutive rows of a workgroup use alternate halves, so each
+    // reduction needs one barrier: a half is rewritten two rows later, after
+    // every wave has passed the barriers of the row in between.
+    __shared__ float red[2][3][kRowsPerWg * WPR];
 
     const int sub = threadIdx.x / kRowLanes;
     const int lr = threadIdx.x % kRowLanes;
     const int wave = lr / kWave;
     const int lane = threadIdx.x % kWave;
-    const bool full = cols >= int64_t(kRowLanes) * E;  // every value of every lane is a column
+    const int slot = sub * WPR;
+    static_assert(!FULL || VEC, "full rows are a vector-layout case");
+    // the column count as the masked helpers see it: a compile-time constant
+    // for full rows, so their masked paths fold away
+    const int64_t span_cols = FULL ? int64_t(kRowLanes) * E : cols;
+    const bool full = span_cols >= int64_t(kRowLanes) * E;  // every value of every lane is a column
     const float n = static_cast<float>(cols);
     const char* gp = static_cast<const char*>(gamma);
     const char* bp = static_cast<const char*>(beta);
 
+    // this lane's gamma and beta (1 and 0 where absent; columns past the row
+    // end are computed but never stored, so their values do not matter)
+    float g[kHold ? E : 1], b[kHold ? E : 1];
+    if constexpr (kHold) {
+        if (gp && bp) {
+            load_span2<IO, VPL, kRowLanes, VEC>(gp, bp, span_cols, 0, lr, g, b, 0.0f);
+        } else {
+#pragma unroll
+            for (int i = 0; i < E; ++i) {
+                g[i] = 1.0f;
+                b[i] = 0.0f;
+            }
+            if (gp) load_span<IO, VPL, kRowLanes, VEC>(gp, span_cols, 0, lr, g, 1.0f);
+            if (bp) load_span<IO, VPL, kRowLanes, VEC>(bp, span_cols, 0, lr, b, 0.0f);
+        }
+    }
+
+    int par = 0;
     for (int64_t rb = int64_t(blockIdx.x) * kRowsPerWg; rb < rows;
-         rb += int64_t(gridDim.x) * kRowsPerWg) {
+         rb += int64_t(gridDim.x) * kRowsPerWg, par ^= 1) {
         const int64_t row = rb + sub;
         const bool active = row < rows;
         float v[E];
         if (active) {
-            load_span<IO, VPL, kRowLanes, VEC, NT>(row_ptr<IO>(x, row, ldx), cols, 0, lr, v, 0.0f);
+            load_span<IO, VPL, kRowLanes, VEC, NT>(row_ptr<IO>(x, row, ldx), span_cols, 0, lr, v,
+                                                  0.0f);
         } else {
 #pragma unroll
             for (int i = 0; i < E; ++i) v[i] = 0.0f;
@@ -59,12 +127,11 @@ __global__ __launch_bounds__(reg_threads<WPR>()) void layernorm_reg_kernel(
         for (int i = 0; i < E; ++i) s += v[i];
         s = wave_sum(s);
         if constexpr (WPR > 1) {
-            if (lane == 0) red[0][sub * WPR + wave] = s;
+            if (lane == 0) red[par][0][slot + wave] = s;
             __syncthreads();
-            s = red[0][sub * WPR];
+            s = red[par][0][slot];
 #pragma unroll
-            for (int w = 1; w < WPR; ++w) s += red[0][sub * WPR + w];
-            __syncthreads();
+            for (int w = 1; w < WPR; ++w) s += red[par][0][slot + w];
         }
         const float mu = s / n;
 
@@ -80,12 +147,11 @@ __global__ __launch_bounds__(reg_threads<WPR>()) void layernorm_reg_kernel(
                 q = fmaf(d, d, q);
             }
         } else {
+            // rows held on chip are at most 65536 columns: 32-bit columns
             const int ncols = static_cast<int>(cols);
 #pragma unroll
             for (int i = 0; i < E; ++i) {
-                // column of value i: vector layout (i / V * lanes + lane) * V + i % V,
-                // scalar layout i * lanes + lane
-                const int col = VEC ? ((i / V) * kRowLanes + lr) * V + i % V : i * kRowLanes + lr;
+                const int col = static_cast<int>(span_col<IO, kRowLanes, VEC>(i, lr));
                 const float d = col < ncols ? v[i] - mu : 0.0f;
                 v[i] = d;
                 a += d;
@@ -96,73 +162,47 @@ __global__ __launch_bounds__(reg_threads<WPR>()) void layernorm_reg_kernel(
         q = wave_sum(q);
         if constexpr (WPR > 1) {
             if (lane == 0) {
-                red[0][sub * WPR + wave] = a;
-                red[1][sub * WPR + wave] = q;
+                red[par][1][slot + wave] = a;
+                red[par][2][slot + wave] = q;
             }
             __syncthreads();
-            a = red[0][sub * WPR];
-            q = red[1][sub * WPR];
+            a = red[par][1][slot];
+            q = red[par][2][slot];
 #pragma unroll
             for (int w = 1; w < WPR; ++w) {
-                a += red[0][sub * WPR + w];
-                q += red[1][sub * WPR + w];
+                a += red[par][1][slot + w];
+                q += red[par][2][slot + w];
             }
-            __syncthreads();
         }
         const float c = a / n;
         const float var = fmaxf(q / n - c * c, 0.0f);
         const float rstd = 1.0f / sqrtf(var + eps);
+        const float off = -c * rstd;  // (d - c) rstd = d rstd + off
 
-        // normalise, gamma and beta, optional GELU, write back -- one
-        // 16-byte vector (or, on the scalar layout, eight values) at a time,
-        // which keeps the epilogue's temporaries to one vector of registers
-        char* yr = row_ptr<IO>(y, row, ldy);
-        constexpr int kChunk = VEC ? V : (E < 8 ? E : 8);  // divides E (E = VPL * V)
-        static_assert(E % kChunk == 0, "chunks cover the lane's values");
-        // columns of value e of chunk k: c0 + e (vector layout: one 16-byte
-        // vector) or c0 + e * kRowLanes (scalar layout); rows held on chip
-        // are at most 65536 columns, so 32-bit column indices suffice
-        constexpr int kStep = VEC ? 1 : kRowLanes;
-        const int ncols = static_cast<int>(cols);
+        // normalise, gamma and beta (two fused multiply-adds), optional GELU,
+        // one chunk of V values (a 16-byte vector on the vector layout) at a
+        // time, in place; then the row is stored
 #pragma unroll
-        for (int k = 0; k < E / kChunk; ++k) {
-            const int c0 = VEC ? (k * kRowLanes + lr) * V : k * kChunk * kRowLanes + lr;
-            float t[kChunk], gv[kChunk], bv[kChunk];
+        for (int k = 0; k < VPL; ++k) {
+            float gk[V], bk[V];
+            if constexpr (kHold) {
 #pragma unroll
-            for (int e = 0; e < kChunk; ++e) {
-                t[e] = (v[k * kChunk + e] - c) * rstd;
-                gv[e] = 1.0f;
-                bv[e] = 0.0f;
-            }
-            const bool whole = VEC && c0 + kChunk <= ncols;  // an unmasked 16-byte vector
-            if (whole) {
-                if (gp) IO::unpack(ld16<false>(reinterpret_cast<const u32x4*>(gp + int64_t(c0) * IO::kBytes)), gv);
-                if (bp) IO::unpack(ld16<false>(reinterpret_cast<const u32x4*>(bp + int64_t(c0) * IO::kBytes)), bv);
-            } else {
-#pragma unroll
-                for (int e = 0; e < kChunk; ++e) {
-                    const int col = c0 + e * kStep;
-                    if (gp && col < ncols) gv[e] = IO::load1(gp, col);
-                    if (bp && col < ncols) bv[e] = IO::load1(bp, col);
+                for (int e = 0; e < V; ++e) {
+                    gk[e] = g[k * V + e];
+                    bk[e] = b[k * V + e];
                 }
+            } else {
+                affine_chunk<IO, kRowLanes, VEC>(gp, bp, span_cols, lr, k, gk, bk);
             }
+            float t[V];
 #pragma unroll
-            for (int e = 0; e < kChunk; ++e) {
-                if (gp) t[e] *= gv[e];
-                if (bp) t[e] += bv[e];
-            }
+            for (int e = 0; e < V; ++e) t[e] = fmaf(fmaf(v[k * V + e], rstd, off), gk[e], bk[e]);
             if constexpr (GELU) gelu_tanh_n(t);
-            if (!active) continue;
-            if (whole) {
-                st16<NT>(reinterpret_cast<u32x4*>(yr + int64_t(c0) * IO::kBytes), IO::pack(t));
-            } else {
 #pragma unroll
-                for (int e = 0; e < kChunk; ++e) {
-                    const int col = c0 + e * kStep;
-                    if (col < ncols) IO::store1(yr, col, t[e]);
-                }
-            }
+            for (int e = 0; e < V; ++e) v[k * V + e] = t[e];
         }
+        if (active)
+            store_span<IO, VPL, kRowLanes, VEC, NT>(row_ptr<IO>(y, row, ldy), span_cols, 0, lr, v);
     }
 }
 

@@ -44,7 +44,10 @@ __device__ inline char* row_ptr(void* p, int64_t row, int64_t ld) {
 // column c0. VEC layout: vectors k*LANES + lane (16-byte loads); scalar
 // layout: columns k*LANES + lane. Columns >= cols read as `fill` (-inf for
 // the max/exp reductions, 0 for sums). A span that lies entirely inside the
-// row (a uniform test) takes the unmasked path.
+// row (a uniform test) takes the unmasked path, whose loads are all issued
+// before any of them is unpacked: left to itself the instruction scheduler
+// interleaves the unpacking with the loads and waits for each load before
+// issuing the next, which serialises their HBM latencies.
 template <class IO, int VPL, int LANES, bool VEC, bool NT = false>
 __device__ inline void load_span(const char* xr, int64_t cols, int64_t c0, int lane,
                                  float (&v)[VPL * IO::kVec], float fill = -__builtin_inff()) {
@@ -57,6 +60,7 @@ __device__ inline void load_span(const char* xr, int64_t cols, int64_t c0, int l
             for (int k = 0; k < VPL; ++k)
                 w[k] = ld16<NT>(reinterpret_cast<const u32x4*>(
                     xr + (c0 + (int64_t(k) * LANES + lane) * V) * IO::kBytes));
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int k = 0; k < VPL; ++k) IO::unpack(w[k], &v[k * V]);
             return;
@@ -80,6 +84,36 @@ __device__ inline void load_span(const char* xr, int64_t cols, int64_t c0, int l
             v[k] = c < cols ? IO::load1(xr, c) : fill;
         }
     }
+}
+
+// Two spans of the same columns from two rows (e.g. y and dy): on the
+// unmasked path all loads of both are in flight before any is unpacked.
+template <class IO, int VPL, int LANES, bool VEC, bool NT = false>
+__device__ inline void load_span2(const char* ar, const char* br, int64_t cols, int64_t c0,
+                                  int lane, float (&va)[VPL * IO::kVec],
+                                  float (&vb)[VPL * IO::kVec], float fill) {
+    constexpr int V = IO::kVec;
+    constexpr int64_t kSpan = int64_t(VPL) * LANES * V;
+    if constexpr (VEC) {
+        if (cols - c0 >= kSpan) {
+            u32x4 wa[VPL], wb[VPL];
+#pragma unroll
+            for (int k = 0; k < VPL; ++k) {
+                const int64_t off = (c0 + (int64_t(k) * LANES + lane) * V) * IO::kBytes;
+                wa[k] = ld16<NT>(reinterpret_cast<const u32x4*>(ar + off));
+                wb[k] = ld16<NT>(reinterpret_cast<const u32x4*>(br + off));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < VPL; ++k) {
+                IO::unpack(wa[k], &va[k * V]);
+                IO::unpack(wb[k], &vb[k * V]);
+            }
+            return;
+        }
+    }
+    load_span<IO, VPL, LANES, VEC, NT>(ar, cols, c0, lane, va, fill);
+    load_span<IO, VPL, LANES, VEC, NT>(br, cols, c0, lane, vb, fill);
 }
 
 // Column (relative to the span start) of value i of a lane in load_span's

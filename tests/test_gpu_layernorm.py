@@ -89,8 +89,10 @@ def run(x, dt, g=None, b=None, gelu=False, eps=1e-5):
     return got
 
 
-COLS = [1, 2, 3, 63, 64, 65, 255, 256, 1000, 1023, 1025, 4095, 4096, 4097, 8193, 16384, 32768,
-        65536]
+# ragged widths, and every width that fills a row shape exactly (256 * 2^k:
+# the unmasked kernel variant) for both dtypes
+COLS = [1, 2, 3, 63, 64, 65, 255, 256, 512, 1000, 1023, 1024, 1025, 2048, 4095, 4096, 4097, 8192,
+        8193, 16384, 32768, 65536]
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
@@ -110,14 +112,18 @@ def test_layernorm_widths(dt, cols):
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-def test_layernorm_without_affine_and_eps(dt):
-    x = random_input((33, 777), dt, 0.01, seed=5)
+@pytest.mark.parametrize("cols", [777, 1024])
+def test_layernorm_without_affine_and_eps(dt, cols):
+    x = random_input((33, cols), dt, 0.01, seed=5)
     for eps in (0.0, 1e-5, 0.1):
         ref = oracle.layernorm_rows(x, eps=eps)
-        assert_ln(run(x, dt, eps=eps), ref, dt, 777, None, None, False, f"no affine eps={eps}")
-    g, _ = params(777, dt, 6)
+        assert_ln(run(x, dt, eps=eps), ref, dt, cols, None, None, False, f"no affine eps={eps}")
+    g, b = params(cols, dt, 6)
     ref = oracle.layernorm_rows(x, g, None)
-    assert_ln(run(x, dt, g, None), ref, dt, 777, as_f32(g, dt), None, False, "gamma only")
+    assert_ln(run(x, dt, g, None), ref, dt, cols, as_f32(g, dt), None, False, "gamma only")
+    ref = oracle.layernorm_rows(x, None, b, gelu=True)
+    assert_ln(run(x, dt, None, b, gelu=True), ref, dt, cols, None, as_f32(b, dt), True,
+              "beta only")
 
 
 def test_ln1_full_size_fp32_shifted_rows():
