@@ -9,6 +9,10 @@ namespace fk {
 
 int64_t attention_head_dim() { return kAttnD; }
 
+int64_t attention_workgroups(int64_t B, int64_t H, int64_t T) {
+    return (T + kAttnBQ - 1) / kAttnBQ * B * H;
+}
+
 hipError_t launch_attention_fwd(const void* q, const void* k, const void* v, void* o, int64_t B,
                                 int64_t H, int64_t T, const int64_t* strides, int causal,
                                 hipStream_t s) {
@@ -26,11 +30,10 @@ hipError_t launch_attention_fwd(const void* q, const void* k, const void* v, voi
     a.ob = strides[9]; a.oh = strides[10]; a.ot = strides[11];
     a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(double(kAttnD)));
     a.causal = causal;
-    const int64_t nqb = (T + kAttnBQ - 1) / kAttnBQ;
+    const int64_t nwg = attention_workgroups(B, H, T);  // <= 2^23, checked by the caller
     void* args[] = {&a};
     return hipLaunchKernel(reinterpret_cast<const void*>(&attention_fwd_kernel),
-                           dim3(static_cast<unsigned>(nqb), static_cast<unsigned>(B * H)),
-                           dim3(kAttnThreads), args, 0, s);
+                           dim3(static_cast<unsigned>(nwg)), dim3(kAttnThreads), args, 0, s);
 }
 
 }  // namespace fk

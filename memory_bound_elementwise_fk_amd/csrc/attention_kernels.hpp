@@ -59,16 +59,25 @@ struct AttnArgs {
     int causal;
 };
 
-typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __global__ __launch_bounds__(kAttnThreads) void attention_fwd_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kAttnBC * kKStride];
     __shared__ __attribute__((aligned(16))) uint16_t Vt[2][kAttnD * kVtStride];
 
+    // One workgroup per (query block, head), numbered level by level with the
+    // heads fastest: level 0 holds every head's longest causal block. The
+    // hardware deals workgroup IDs round-robin to its partitions (8 XCDs,
+    // each split again), so with the heads fastest every partition gets the
+    // same mix of long and short causal blocks, longest first. (Numbered with
+    // the query blocks fastest, a multiple of 32 of them put the same block
+    // position in the same partition every time, and causal attention took as
+    // long as full attention.)
     const int64_t nqb = (a.T + kAttnBQ - 1) / kAttnBQ;
-    // longest causal blocks first: query block nqb - 1 - blockIdx.x
-    const int64_t qblk = a.causal ? nqb - 1 - blockIdx.x : blockIdx.x;
-    const int64_t bh = blockIdx.y;
+    const int64_t BH = a.B * a.H;
+    const int64_t lev = int64_t(blockIdx.x) / BH;
+    const int64_t bh = int64_t(blockIdx.x) - lev * BH;
+    const int64_t qblk = a.causal ? nqb - 1 - lev : lev;
     const int64_t b = bh / a.H, h = bh % a.H;
     const uint16_t* Q = a.q + b * a.qb + h * a.qh;
     const uint16_t* Kg = a.k + b * a.kb + h * a.kh;
@@ -166,80 +175,90 @@ __global__ __launch_bounds__(kAttnThreads) void attention_fwd_kernel(AttnArgs a)
         const int64_t kb0 = kb * kAttnBC;
         if (kb + 1 < nkb) load_block(kb0 + kAttnBC);
 
-        // S^T for the block's two 32-key tiles
-        f32x16 s[2];
+        // a causal block wholly above this wave's queries contributes nothing
+        // (its last key block can be): the wave skips it (uniform branch)
+        if (!(a.causal && kb0 > q0 + 31)) {
+            // S^T for the block's two 32-key tiles
+            f32x16 s[2];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            s[t] = f32x16{};
-            const uint16_t* kbase = &Ks[buf][(t * 32 + lane % 32) * kKStride + g * 8];
+            for (int t = 0; t < 2; ++t) {
+                s[t] = f32x16{};
+                const uint16_t* kbase = &Ks[buf][(t * 32 + lane % 32) * kKStride + g * 8];
 #pragma unroll
-            for (int kk = 0; kk < kAttnD / 16; ++kk)
-                s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    *reinterpret_cast<const bf16x8*>(kbase + kk * 16), qf[kk], s[t], 0, 0, 0);
-        }
-
-        // scale to log2 units, mask, block max over the query's 32 keys
-        float bm = -__builtin_inff();
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int64_t key = kb0 + t * 32 + (v / 4) * 8 + g * 4 + v % 4;
-                float x = s[t][v] * a.scale_log2;
-                if (key >= a.T || (a.causal && key > myq)) x = -__builtin_inff();
-                s[t][v] = x;
-                bm = fmaxf(bm, x);
+                for (int kk = 0; kk < kAttnD / 16; ++kk)
+                    s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        *reinterpret_cast<const bf16x8*>(kbase + kk * 16), qf[kk], s[t], 0, 0, 0);
             }
-        }
-        bm = fmaxf(bm, __shfl_xor(bm, 32));
-        const float mn = fmaxf(m, bm);
-        // while every key seen is masked (mn = -inf) nothing accumulates
-        const float base = mn == -__builtin_inff() ? 0.0f : mn;
-        const float corr = (m == mn) ? 1.0f : exp2_raw(m - base);
-        float bs = 0.0f;
-        bf16x8 pf[4];  // P^T fragments: chunk 2 t + c of tile t
+
+            // mask (only blocks that reach past T or, causal, past the wave's
+            // first query), then the block max over the query's 32 keys, in
+            // raw score units (the scale is positive)
+            if (kb0 + kAttnBC > a.T || (a.causal && kb0 + kAttnBC - 1 > q0)) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+                for (int t = 0; t < 2; ++t) {
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                float pv[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    pv[e] = exp2_raw(s[t][c * 8 + e] - base);
-                    bs += pv[e];
+                    for (int v = 0; v < 16; ++v) {
+                        const int64_t key = kb0 + t * 32 + (v / 4) * 8 + g * 4 + v % 4;
+                        if (key >= a.T || (a.causal && key > myq)) s[t][v] = -__builtin_inff();
+                    }
                 }
-                u32x4 w;
-                w.x = IoBF16::cvt2(pv[0], pv[1]);
-                w.y = IoBF16::cvt2(pv[2], pv[3]);
-                w.z = IoBF16::cvt2(pv[4], pv[5]);
-                w.w = IoBF16::cvt2(pv[6], pv[7]);
-                pf[t * 2 + c] = __builtin_bit_cast(bf16x8, w);
             }
-        }
-        bs += __shfl_xor(bs, 32);
-        l = l * corr + bs;
-        m = mn;
+            float bm = -__builtin_inff();
 #pragma unroll
-        for (int dt = 0; dt < kAttnD / 32; ++dt) acc[dt] *= corr;
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) bm = fmaxf(bm, s[t][v]);
+            bm = fmaxf(bm, __shfl_xor(bm, 32)) * a.scale_log2;
+            const float mn = fmaxf(m, bm);
+            // while every key seen is masked (mn = -inf) nothing accumulates
+            const float base = mn == -__builtin_inff() ? 0.0f : mn;
+            const float corr = (m == mn) ? 1.0f : exp2_raw(m - base);
+            float bs = 0.0f;
+            bf16x8 pf[4];  // P^T fragments: chunk 2 t + c of tile t
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    float pv[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        // 2^(s scale - base): the scale folded into one fma
+                        pv[e] = exp2_raw(fmaf(s[t][c * 8 + e], a.scale_log2, -base));
+                        bs += pv[e];
+                    }
+                    u32x4 w;
+                    w.x = IoBF16::cvt2(pv[0], pv[1]);
+                    w.y = IoBF16::cvt2(pv[2], pv[3]);
+                    w.z = IoBF16::cvt2(pv[4], pv[5]);
+                    w.w = IoBF16::cvt2(pv[6], pv[7]);
+                    pf[t * 2 + c] = __builtin_bit_cast(bf16x8, w);
+                }
+            }
+            bs += __shfl_xor(bs, 32);
+            l = l * corr + bs;
+            // rescale the accumulators only when some lane's max grew (after
+            // the first blocks it rarely does; multiplying by 1 is a no-op)
+            if (__builtin_amdgcn_ballot_w64(m != mn) != 0) {
+#pragma unroll
+                for (int dt = 0; dt < kAttnD / 32; ++dt) acc[dt] *= corr;
+            }
+            m = mn;
 
-        // O^T += V^T P^T; V^T fragment of d-tile dt, chunk (t, c): dims
-        // dt * 32 + lane % 32, keys t * 32 + 16 c + 4 g + {0..3} and + 8
+            // O^T += V^T P^T; V^T fragment of d-tile dt, chunk (t, c): dims
+            // dt * 32 + lane % 32, keys t * 32 + 16 c + 4 g + {0..3} and + 8,
+            // read as two 8-byte runs (pairs of keys per 32-bit word)
 #pragma unroll
-        for (int dt = 0; dt < kAttnD / 32; ++dt) {
-            const uint16_t* vrow = &Vt[buf][(dt * 32 + lane % 32) * kVtStride + 4 * g];
+            for (int dt = 0; dt < kAttnD / 32; ++dt) {
+                const uint16_t* vrow = &Vt[buf][(dt * 32 + lane % 32) * kVtStride + 4 * g];
 #pragma unroll
-            for (int ch = 0; ch < 4; ++ch) {
-                const int k0 = (ch / 2) * 32 + (ch % 2) * 16;
-                const u16x4 lo = *reinterpret_cast<const u16x4*>(vrow + k0);
-                const u16x4 hi = *reinterpret_cast<const u16x4*>(vrow + k0 + 8);
-                const uint16_t vv[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-                u32x4 w;
-                w.x = vv[0] | (uint32_t(vv[1]) << 16);
-                w.y = vv[2] | (uint32_t(vv[3]) << 16);
-                w.z = vv[4] | (uint32_t(vv[5]) << 16);
-                w.w = vv[6] | (uint32_t(vv[7]) << 16);
-                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w),
-                                                                  pf[ch], acc[dt], 0, 0, 0);
+                for (int ch = 0; ch < 4; ++ch) {
+                    const int k0 = (ch / 2) * 32 + (ch % 2) * 16;
+                    const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + k0);
+                    const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + k0 + 8);
+                    const u32x4 w = {lo.x, lo.y, hi.x, hi.y};
+                    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, w), pf[ch], acc[dt], 0, 0, 0);
+                }
             }
         }
 

@@ -256,7 +256,10 @@ def test_attention_validation(L):
     odd = st(*([2 * 3 * 136, 3 * 136, 132] * 4))       # stride not a multiple of 8
     assert f(A, B, C, D, 2, 3, 16, 128, odd, 1, bf, None) == fk.FK_ERR_UNSUPPORTED
     assert f(A, B, C, A + 256, 2, 3, 16, 128, good, 1, bf, None) == fk.FK_ERR_OVERLAP
-    assert f(A, B, C, D, 300, 300, 16, 128, good, 1, bf, None) == fk.FK_ERR_UNSUPPORTED  # B*H
+    # more than 2^23 workgroups (B * H * ceil(T / 128))
+    assert f(A, B, C, D, 3000, 3000, 16, 128, good, 1, bf, None) == fk.FK_ERR_UNSUPPORTED
+    assert f(A, B, C, D, 64, 1024, 128 * 129, 128, good, 1, bf, None) == fk.FK_ERR_UNSUPPORTED
+    assert f(A, B, C, D, 1, 1, 1 << 31, 128, good, 1, bf, None) == fk.FK_ERR_UNSUPPORTED
 
 
 def test_copy_validation(L):
