@@ -61,7 +61,12 @@ struct AttnArgs {
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-__global__ __launch_bounds__(kAttnThreads) void attention_fwd_kernel(AttnArgs a) {
+// Two waves per SIMD (two workgroups per CU; LDS 70 KiB each): with one, a
+// wave's MFMA, exponential and LDS phases run back to back and the K/V loads
+// barely overlap them; the second workgroup fills those gaps. The compiler
+// fits the kernel in 256 registers (no AGPRs, no spills) when asked to.
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attention_fwd_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kAttnBC * kKStride];
     __shared__ __attribute__((aligned(16))) uint16_t Vt[2][kAttnD * kVtStride];
 
