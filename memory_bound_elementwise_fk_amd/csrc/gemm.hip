@@ -5,11 +5,13 @@
 namespace fk {
 namespace {
 
-// 256 x 256 output tiles, K steps of 64, four waves of 128 x 128: the
-// fastest of the shapes measured on MI355X for an 8192 x 16384 x 4096
-// product (128 x 128, 128 x 256, 256 x 128 tiles and K steps of 32 were
-// 0-25 % slower).
-using LinearShape = GemmShape<256, 256, 64, 128, 128>;
+// 256 x 256 output tiles, K steps of 64, eight waves of 64 x 128 at two
+// waves per SIMD (241 VGPRs, no spills): the fastest of the shapes measured
+// on MI355X for an 8192 x 16384 x 4096 product. Four waves of 128 x 128 (one
+// per SIMD, 512 registers) were 15-20 % slower: a lone wave leaves the
+// matrix cores idle while it waits on LDS and the barrier; 128 x 128 tiles
+// (two workgroups per CU) and K steps of 32 were 5-10 % slower.
+using LinearShape = GemmShape<256, 256, 64, 64, 128, 2>;
 constexpr int64_t kMaxWorkItems = int64_t(1) << 31;
 
 }  // namespace

@@ -14,7 +14,7 @@
 //
 // Block tile BM x BN, K step BK; the block's waves form a (BM/WM) x (BN/WN)
 // grid, each computing a WM x WN tile as (WM/32) x (WN/32) MFMA 32x32x16
-// tiles. Operand tiles are staged through LDS, double-buffered: the global
+// tiles; the registers are budgeted for OCC waves per SIMD. Operand tiles are staged through LDS, double-buffered: the global
 // loads of step k+1 are in flight while step k is multiplied, and one
 // barrier per step separates the buffers. LDS rows are padded by 16 bytes
 // so the 16-byte fragment reads of 32 consecutive rows do not pile onto the
@@ -33,9 +33,10 @@ namespace fk {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_>
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int OCC_ = 1>
 struct GemmShape {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
+    static constexpr int kOcc = OCC_;  // waves per SIMD the registers are budgeted for
     static constexpr int kWavesM = BM / WM, kWavesN = BN / WN;
     static constexpr int kThreads = kWavesM * kWavesN * kWave;
     static constexpr int kTM = WM / 32, kTN = WN / 32;
@@ -71,7 +72,8 @@ __device__ inline void gemm_tile_of(int64_t b, int64_t tiles_m, int64_t tiles_n,
 }
 
 template <class S>
-__global__ __launch_bounds__(S::kThreads) void linear_gelu_kernel(
+__global__ __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(S::kOcc, S::kOcc)))
+void linear_gelu_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K,
     int64_t ldx, int64_t ldw, int64_t ldy, int gelu) {
