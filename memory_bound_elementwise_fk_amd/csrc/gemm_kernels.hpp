@@ -55,7 +55,7 @@ struct GemmShape {
 // first remapped so that each XCD works through a contiguous range of the
 // ordering below, then tiles are visited in column-strips of kGroup tile
 // rows, so the blocks in flight on one XCD share operand tiles in its L2.
-constexpr int kGemmGroup = 16;
+constexpr int kGemmGroup = 4;  // measured best of 4, 8, 16, 32 for 8192 x 16384 x 4096
 constexpr int kXcds = 8;
 
 __device__ inline void gemm_tile_of(int64_t b, int64_t tiles_m, int64_t tiles_n, int64_t& tm,
@@ -179,6 +179,182 @@ void linear_gelu_kernel(
         }
         if (kt + 1 < nk) store_tiles(buf ^ 1);
         __syncthreads();
+    }
+
+    // epilogue: + bias, GELU on the accumulators, round to bf16, store
+#pragma unroll
+    for (int j = 0; j < S::kTN; ++j) {
+        const int64_t col = n0 + wn * S::WN + j * 32 + lane % 32;
+        const float bv = (bias != nullptr && col < N) ? IoBF16::load1(bias, col) : 0.0f;
+#pragma unroll
+        for (int i = 0; i < S::kTM; ++i) {
+            float v[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) v[e] = acc[i][j][e] + bv;
+            if (gelu) gelu_tanh_n(v);
+            const int64_t row0 = m0 + wm * S::WM + i * 32 + (lane / 32) * 4;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int64_t row = row0 + (e / 4) * 8 + e % 4;
+                if (row < M && col < N) IoBF16::store1(Y, row * ldy + col, v[e]);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Main loop fed by direct global -> LDS loads (global_load_lds_dwordx4: lane
+// i of a wave writes its 16 bytes at LDS base + 16 i, no registers and no
+// LDS store instructions). Operand tiles go through a ring of kStages LDS
+// stages, loaded kStages - 1 K steps ahead; each step waits for its own
+// stage with a counted wait on the loads still in flight, then one barrier.
+//
+// LDS layout of a stage: A rows then B rows, each row BK bf16 = 4 chunks of
+// 16 bytes, chunk c of row r stored at chunk position c ^ ((r >> 2) & 3) of
+// the row. The MFMA fragment reads (32 consecutive rows, one chunk) then
+// spread over all 16 bank groups of 16 bytes. A wave's direct load fills 16
+// rows (1 KiB), so lane i fetches row i / 4, chunk (i & 3) ^ ((i >> 4) & 3).
+//
+// Rows past M or N load row M - 1 or N - 1 instead (valid memory; those
+// outputs are never stored). K must be a multiple of BK.
+template <int BM_, int BN_, int WM_, int WN_, int OCC_, int STAGES_>
+struct DtlShape {
+    static constexpr int BM = BM_, BN = BN_, BK = 32, WM = WM_, WN = WN_;
+    static constexpr int kOcc = OCC_, kStages = STAGES_;
+    static constexpr int kWavesM = BM / WM, kWavesN = BN / WN;
+    static constexpr int kWaves = kWavesM * kWavesN;
+    static constexpr int kThreads = kWaves * kWave;
+    static constexpr int kTM = WM / 32, kTN = WN / 32;
+    static constexpr int kRowBytes = BK * 2;                      // 64
+    static constexpr int kStageBytes = (BM + BN) * kRowBytes;
+    static constexpr int kLoadsPerWave = (BM + BN) / 16 / kWaves;  // 1 KiB wave loads per step
+    static_assert((BM + BN) % (16 * kWaves) == 0, "whole wave loads");
+    static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "tiles");
+    static_assert(kStages >= 2 && kStages * kStageBytes <= 160 * 1024, "LDS");
+};
+
+typedef __attribute__((address_space(3))) void* las_ptr;
+
+// One direct 16-byte load per lane into LDS at lds_base + 16 * lane. Issued
+// from inline assembly so that the compiler does not track it: its own
+// tracking of such loads waits for all of them (vmcnt(0)) before every
+// barrier and every LDS read, which would serialise the stage ring. The
+// kernel waits for them itself (vmcnt_imm); "memory" keeps the compiler from
+// moving LDS reads across the statement or treating the LDS as unwritten.
+// M0 is a register the compiler reserves; it warns that a clobber of it is
+// not saved. Nothing else in these kernels uses M0 (gfx9 LDS instructions do
+// not), so it is only ever set here, right before the load that reads it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ inline void lds_dma16(const void* gsrc, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gsrc), "s"(lds_base)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt immediate waiting for at most n outstanding vector memory
+// operations (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt
+// left at their maxima, i.e. not waited for)
+__device__ constexpr int vmcnt_imm(int n) {
+    return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+}
+
+template <class S>
+__global__ __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(S::kOcc, S::kOcc)))
+void linear_gelu_dtl_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
+                            const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y,
+                            int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldw, int64_t ldy,
+                            int gelu) {
+    __shared__ __attribute__((aligned(1024))) char smem[S::kStages * S::kStageBytes];
+
+    const int64_t tiles_m = (M + S::BM - 1) / S::BM;
+    const int64_t tiles_n = (N + S::BN - 1) / S::BN;
+    int64_t tm, tn;
+    gemm_tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int64_t m0 = tm * S::BM, n0 = tn * S::BN;
+
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int wave = tid / kWave;
+    const int wm = wave / S::kWavesN, wn = wave % S::kWavesN;
+
+    // this lane's source rows for its wave's loads (row groups of 16 of the
+    // stage: A rows 0 .. BM - 1, then B rows), with the chunk swizzle
+    const int lrow = lane / 4;
+    const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);
+    const uint16_t* src[S::kLoadsPerWave];
+#pragma unroll
+    for (int j = 0; j < S::kLoadsPerWave; ++j) {
+        const int grp = wave * S::kLoadsPerWave + j;  // 16-row group of the stage
+        const int r = grp * 16 + lrow;
+        if (r < S::BM) {
+            const int64_t row = m0 + r < M ? m0 + r : M - 1;
+            src[j] = X + row * ldx + lchunk * 8;
+        } else {
+            const int64_t row = n0 + (r - S::BM) < N ? n0 + (r - S::BM) : N - 1;
+            src[j] = W + row * ldw + lchunk * 8;
+        }
+    }
+    auto issue = [&](int64_t kt) {  // loads of K step kt into stage kt % kStages
+        char* stage = smem + (kt % S::kStages) * S::kStageBytes;
+#pragma unroll
+        for (int j = 0; j < S::kLoadsPerWave; ++j) {
+            const int grp = wave * S::kLoadsPerWave + j;
+            // LDS byte address of the wave's 1 KiB (wave-uniform: an SGPR)
+            const uint32_t dst = __builtin_amdgcn_readfirstlane(
+                static_cast<uint32_t>(reinterpret_cast<uintptr_t>((las_ptr)(stage + grp * 1024))));
+            lds_dma16(src[j] + kt * S::BK, dst);
+        }
+    };
+
+    f32x16 acc[S::kTM][S::kTN];
+#pragma unroll
+    for (int i = 0; i < S::kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < S::kTN; ++j) acc[i][j] = f32x16{};
+
+    const int64_t nk = K / S::BK;
+#pragma unroll
+    for (int st = 0; st < S::kStages - 1; ++st)
+        if (st < nk) issue(st);
+
+    // fragment rows of this lane and the swizzled chunk offsets per kk
+    const int frow = lane % 32;
+    for (int64_t kt = 0; kt < nk; ++kt) {
+        // stage kt landed: at most (kStages - 2) later steps' loads in flight
+        if (kt + S::kStages - 2 < nk)
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm((S::kStages - 2) * S::kLoadsPerWave));
+        else
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __syncthreads();  // every wave's part of stage kt; stage kt - 1 free
+        if (kt + S::kStages - 1 < nk) issue(kt + S::kStages - 1);
+
+        const char* stage = smem + (kt % S::kStages) * S::kStageBytes;
+#pragma unroll
+        for (int kk = 0; kk < S::BK / 16; ++kk) {
+            const int c = kk * 2 + lane / 32;  // logical chunk of this lane's 8 k values
+            bf16x8 af[S::kTM], bf[S::kTN];
+#pragma unroll
+            for (int i = 0; i < S::kTM; ++i) {
+                const int r = wm * S::WM + i * 32 + frow;
+                af[i] = *reinterpret_cast<const bf16x8*>(stage + r * S::kRowBytes +
+                                                         ((c ^ ((r >> 2) & 3)) << 4));
+            }
+#pragma unroll
+            for (int j = 0; j < S::kTN; ++j) {
+                const int r = S::BM + wn * S::WN + j * 32 + frow;
+                bf[j] = *reinterpret_cast<const bf16x8*>(stage + r * S::kRowBytes +
+                                                         ((c ^ ((r >> 2) & 3)) << 4));
+            }
+#pragma unroll
+            for (int i = 0; i < S::kTM; ++i)
+#pragma unroll
+                for (int j = 0; j < S::kTN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j],
+                                                                        0, 0, 0);
+        }
     }
 
     // epilogue: + bias, GELU on the accumulators, round to bf16, store

@@ -51,8 +51,12 @@ def check(got, x, w, b, gelu, what, rows=None):
     assert within >= 0.99, f"{what}: only {within:.4f} of outputs within one bf16 ulp"
 
 
+# K % 32 == 0 takes the direct-to-LDS kernel (rows past M or N clamped),
+# other K the register-staged one
 @pytest.mark.parametrize("M,N,K", [(1, 1, 8), (7, 13, 24), (300, 200, 392), (256, 256, 64),
-                                   (257, 511, 520), (512, 768, 1024), (1000, 300, 8)])
+                                   (257, 511, 520), (512, 768, 1024), (1000, 300, 8),
+                                   (1, 1, 32), (33, 65, 96), (300, 200, 384), (257, 511, 1024),
+                                   (513, 257, 4096)])
 @pytest.mark.parametrize("gelu", [True, False])
 def test_linear_shapes(M, N, K, gelu):
     x, w, b = operands(M, N, K, seed=M * 7 + N + K)
@@ -72,8 +76,9 @@ def test_linear_without_bias_and_k_zero():
     assert np.array_equal(to_host(ye), np.broadcast_to(oracle.gelu_tanh(b), (5, 70)))
 
 
-def test_linear_strided_operands():
-    M, N, K = 300, 260, 136
+@pytest.mark.parametrize("K", [136, 160])  # register-staged / direct-to-LDS kernel
+def test_linear_strided_operands(K):
+    M, N = 300, 260
     x, w, b = operands(M, N, K, seed=5)
     xb = np.zeros((M, K + 8), np.uint16)
     xb[:, :K] = x
