@@ -51,9 +51,12 @@ hipError_t launch_reg(const void* x, void* y, int64_t rows, int64_t cols, int64_
     constexpr int kThreads = reg_threads<WPR>();
     constexpr int kRowsPerWg = kThreads / (WPR * kWave);
     const int64_t grid = clamp_grid((rows + kRowsPerWg - 1) / kRowsPerWg, kThreads);
+    // a row that fills the shape exactly runs the variant without masks
+    const bool full = vec && cols == reg_capacity<IO>(RegShape{WPR, VPL});
     const void* fn =
-        vec ? reinterpret_cast<const void*>(&softmax_reg_kernel<IO, WPR, VPL, true, kRowNT>)
-            : reinterpret_cast<const void*>(&softmax_reg_kernel<IO, WPR, VPL, false>);
+        full ? reinterpret_cast<const void*>(&softmax_reg_kernel<IO, WPR, VPL, true, kRowNT, true>)
+        : vec ? reinterpret_cast<const void*>(&softmax_reg_kernel<IO, WPR, VPL, true, kRowNT>)
+              : reinterpret_cast<const void*>(&softmax_reg_kernel<IO, WPR, VPL, false>);
     return launch_kernel(fn, grid, kThreads, s, x, y, rows, cols, ldx, ldy);
 }
 

@@ -167,14 +167,23 @@ constexpr int reg_threads() {
 }
 
 // ------------------------------------------------- single-pass kernel -----
-template <class IO, int WPR, int VPL, bool VEC, bool NT = false>
+// FULL: the launcher guarantees cols == WPR * 64 * VPL * V (the row fills the
+// shape exactly, on the vector layout), so no masking code is compiled (the
+// masks of ragged rows otherwise hold enough SGPRs to cost a wave per SIMD).
+template <class IO, int WPR, int VPL, bool VEC, bool NT = false, bool FULL = false>
 __global__ __launch_bounds__(reg_threads<WPR>()) void softmax_reg_kernel(
     const void* x, void* y, int64_t rows, int64_t cols, int64_t ldx, int64_t ldy) {
     constexpr int V = IO::kVec;
     constexpr int E = VPL * V;
     constexpr int kRowLanes = WPR * kWave;
     constexpr int kRowsPerWg = reg_threads<WPR>() / kRowLanes;
-    __shared__ float red[kRowsPerWg * WPR];
+    static_assert(!FULL || VEC, "full rows are a vector-layout case");
+    // the column count as the masked helpers see it (a constant for full rows)
+    const int64_t span_cols = FULL ? int64_t(kRowLanes) * E : cols;
+    // per-wave partials of the row max ([0]) and sum ([1]); one barrier per
+    // reduction: a slot is rewritten only on the next row, after every wave
+    // has passed the other reduction's barrier, i.e. finished reading it
+    __shared__ float red[2][kRowsPerWg * WPR];
 
     const int sub = threadIdx.x / kRowLanes;  // which row of the WG
     const int lr = threadIdx.x % kRowLanes;   // lane within the row's lanes
@@ -189,7 +198,7 @@ __global__ __launch_bounds__(reg_threads<WPR>()) void softmax_reg_kernel(
         const bool active = row < rows;
         float v[E];
         if (active) {
-            load_span<IO, VPL, kRowLanes, VEC, NT>(row_ptr<IO>(x, row, ldx), cols, 0, lr, v);
+            load_span<IO, VPL, kRowLanes, VEC, NT>(row_ptr<IO>(x, row, ldx), span_cols, 0, lr, v);
         } else {
 #pragma unroll
             for (int i = 0; i < E; ++i) v[i] = kNegInf;
@@ -201,12 +210,11 @@ __global__ __launch_bounds__(reg_threads<WPR>()) void softmax_reg_kernel(
         for (int i = 0; i < E; ++i) m = fmaxf(m, v[i]);
         m = wave_max(m);
         if constexpr (WPR > 1) {
-            if (lane == 0) red[sub * WPR + wave] = m;
+            if (lane == 0) red[0][sub * WPR + wave] = m;
             __syncthreads();
-            m = red[sub * WPR];
+            m = red[0][sub * WPR];
 #pragma unroll
-            for (int w = 1; w < WPR; ++w) m = fmaxf(m, red[sub * WPR + w]);
-            __syncthreads();
+            for (int w = 1; w < WPR; ++w) m = fmaxf(m, red[0][sub * WPR + w]);
         }
 
         // numerators and their sum (masked columns give 2^-inf = 0)
@@ -218,12 +226,11 @@ __global__ __launch_bounds__(reg_threads<WPR>()) void softmax_reg_kernel(
         }
         s = wave_sum(s);
         if constexpr (WPR > 1) {
-            if (lane == 0) red[sub * WPR + wave] = s;
+            if (lane == 0) red[1][sub * WPR + wave] = s;
             __syncthreads();
-            s = red[sub * WPR];
+            s = red[1][sub * WPR];
 #pragma unroll
-            for (int w = 1; w < WPR; ++w) s += red[sub * WPR + w];
-            __syncthreads();
+            for (int w = 1; w < WPR; ++w) s += red[1][sub * WPR + w];
         }
 
         // normalise and write back
@@ -231,7 +238,7 @@ __global__ __launch_bounds__(reg_threads<WPR>()) void softmax_reg_kernel(
 #pragma unroll
         for (int i = 0; i < E; ++i) v[i] *= r;
         if (active)
-            store_span<IO, VPL, kRowLanes, VEC, NT>(row_ptr<IO>(y, row, ldy), cols, 0, lr, v);
+            store_span<IO, VPL, kRowLanes, VEC, NT>(row_ptr<IO>(y, row, ldy), span_cols, 0, lr, v);
     }
 }
 

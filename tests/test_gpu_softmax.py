@@ -67,8 +67,10 @@ def test_c5a_softmax_fp32_full_size_self_managed():
 
 
 # ------------------------------------------------------------- shapes -----
-COLS = [1, 2, 3, 5, 63, 64, 65, 255, 256, 257, 1000, 1023, 1024, 1025, 2047, 2049, 4095,
-        4096, 4097, 8192, 8193, 16385, 32768, 32769, 65536, 65537, 100_003]
+# ragged widths, and every width that fills a single-pass row shape exactly
+# (256 * 2^k: the unmasked kernel variant) for both dtypes
+COLS = [1, 2, 3, 5, 63, 64, 65, 255, 256, 257, 512, 1000, 1023, 1024, 1025, 2047, 2048, 2049,
+        4095, 4096, 4097, 8192, 8193, 16384, 16385, 32768, 32769, 65536, 65537, 100_003]
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
