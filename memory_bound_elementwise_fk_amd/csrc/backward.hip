@@ -64,9 +64,12 @@ hipError_t launch_sbwd(const void* y, const void* dy, void* dx, int64_t rows, in
     constexpr int kRowsPerWg = kThreads / (WPR * kWave);
     int64_t grid = (rows + kRowsPerWg - 1) / kRowsPerWg;
     if (grid > kMaxWorkItems / kThreads) grid = kMaxWorkItems / kThreads;
+    // a row that fills the shape exactly runs the variant without masks
+    const bool full = vec && cols == bwd_capacity<IO>(BwdShape{WPR, VPL});
     const void* fn =
-        vec ? reinterpret_cast<const void*>(&softmax_bwd_reg_kernel<IO, WPR, VPL, true, true>)
-            : reinterpret_cast<const void*>(&softmax_bwd_reg_kernel<IO, WPR, VPL, false>);
+        full ? reinterpret_cast<const void*>(&softmax_bwd_reg_kernel<IO, WPR, VPL, true, true, true>)
+        : vec ? reinterpret_cast<const void*>(&softmax_bwd_reg_kernel<IO, WPR, VPL, true, true>)
+              : reinterpret_cast<const void*>(&softmax_bwd_reg_kernel<IO, WPR, VPL, false>);
     return launch_kernel(fn, grid, kThreads, s, y, dy, dx, rows, cols, ldy, lddy, lddx);
 }
 

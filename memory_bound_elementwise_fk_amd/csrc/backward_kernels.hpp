@@ -86,14 +86,21 @@ __global__ __launch_bounds__(T) void ew2_scalar_kernel(const void* a, const void
 // as softmax_reg_kernel): dot = sum y dy, dx = y (dy - dot). dx may be y or
 // dy exactly (with the same stride): every value is in registers before the
 // row is written.
-template <class IO, int WPR, int VPL, bool VEC, bool NT = false>
+// FULL: the launcher guarantees cols == WPR * 64 * VPL * V (no masking code).
+template <class IO, int WPR, int VPL, bool VEC, bool NT = false, bool FULL = false>
 __global__ __launch_bounds__(reg_threads<WPR>()) void softmax_bwd_reg_kernel(
     const void* y, const void* dy, void* dx, int64_t rows, int64_t cols, int64_t ldy,
     int64_t lddy, int64_t lddx) {
     constexpr int E = VPL * IO::kVec;
     constexpr int kRowLanes = WPR * kWave;
     constexpr int kRowsPerWg = reg_threads<WPR>() / kRowLanes;
-    __shared__ float red[kRowsPerWg * WPR];
+    static_assert(!FULL || VEC, "full rows are a vector-layout case");
+    const int64_t span_cols = FULL ? int64_t(kRowLanes) * E : cols;
+    // per-wave partial dot products, alternating halves row by row: one
+    // barrier per row (a half is rewritten two rows later, after every wave
+    // has passed the barrier of the row in between)
+    __shared__ float red[2][kRowsPerWg * WPR];
+    int par = 0;
 
     const int sub = threadIdx.x / kRowLanes;
     const int lr = threadIdx.x % kRowLanes;
@@ -101,14 +108,14 @@ __global__ __launch_bounds__(reg_threads<WPR>()) void softmax_bwd_reg_kernel(
     const int lane = threadIdx.x % kWave;
 
     for (int64_t rb = int64_t(blockIdx.x) * kRowsPerWg; rb < rows;
-         rb += int64_t(gridDim.x) * kRowsPerWg) {
+         rb += int64_t(gridDim.x) * kRowsPerWg, par ^= 1) {
         const int64_t row = rb + sub;
         const bool active = row < rows;
         float vy[E], vg[E];
         if (active) {
             load_span2<IO, VPL, kRowLanes, VEC, NT>(row_ptr<IO>(y, row, ldy),
-                                                    row_ptr<IO>(dy, row, lddy), cols, 0, lr, vy,
-                                                    vg, 0.0f);
+                                                    row_ptr<IO>(dy, row, lddy), span_cols, 0, lr,
+                                                    vy, vg, 0.0f);
         } else {
 #pragma unroll
             for (int i = 0; i < E; ++i) vy[i] = vg[i] = 0.0f;
@@ -118,17 +125,17 @@ __global__ __launch_bounds__(reg_threads<WPR>()) void softmax_bwd_reg_kernel(
         for (int i = 0; i < E; ++i) d = fmaf(vy[i], vg[i], d);
         d = wave_sum(d);
         if constexpr (WPR > 1) {
-            if (lane == 0) red[sub * WPR + wave] = d;
+            if (lane == 0) red[par][sub * WPR + wave] = d;
             __syncthreads();
-            d = red[sub * WPR];
+            d = red[par][sub * WPR];
 #pragma unroll
-            for (int w = 1; w < WPR; ++w) d += red[sub * WPR + w];
-            __syncthreads();
+            for (int w = 1; w < WPR; ++w) d += red[par][sub * WPR + w];
         }
 #pragma unroll
         for (int i = 0; i < E; ++i) vg[i] = vy[i] * (vg[i] - d);
         if (active)
-            store_span<IO, VPL, kRowLanes, VEC, NT>(row_ptr<IO>(dx, row, lddx), cols, 0, lr, vg);
+            store_span<IO, VPL, kRowLanes, VEC, NT>(row_ptr<IO>(dx, row, lddx), span_cols, 0, lr,
+                                                    vg);
     }
 }
 

@@ -151,7 +151,10 @@ def run_sbwd(y, dy, dt):
     return got
 
 
-SCOLS = [1, 2, 3, 63, 64, 65, 1000, 1023, 1025, 4096, 4097, 8192, 16384, 16385, 32768]
+# ragged widths, and every width that fills a row shape exactly (the
+# unmasked kernel variant) for both dtypes
+SCOLS = [1, 2, 3, 63, 64, 65, 256, 512, 1000, 1023, 1024, 1025, 2048, 4096, 4097, 8192, 16384,
+         16385, 32768]
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
