@@ -152,8 +152,8 @@ def main() -> int:
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall = t1 - t0
-    per_kernel_ms = {name: sum(a.elapsed_time(b) for a, b in ev[name]) / args.steps
-                     for name in STEP}
+    launch_ms = {name: sorted(a.elapsed_time(b) for a, b in ev[name]) for name in STEP}
+    per_kernel_ms = {name: sum(t) / args.steps for name, t in launch_ms.items()}
     value = step_bytes * args.steps / wall / 1e9
     log(f"step {wall / args.steps * 1e3:.3f} ms, {value:.1f} GB/s")
 
@@ -161,7 +161,10 @@ def main() -> int:
     for name in STEP:
         ms = per_kernel_ms[name]
         gbs = kbytes[name] / (ms * 1e-3) / 1e9
-        kernels[name] = {"ms": round(ms, 5), "bytes": kbytes[name], "GBps": round(gbs, 1),
+        t = launch_ms[name]
+        med = t[len(t) // 2] if len(t) % 2 else 0.5 * (t[len(t) // 2 - 1] + t[len(t) // 2])
+        kernels[name] = {"ms": round(ms, 5), "median_ms": round(med, 5), "min_ms": round(t[0], 5),
+                         "bytes": kbytes[name], "GBps": round(gbs, 1),
                          "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
 
     # ---- parity spot check of what was timed (full checks live in tests/)
@@ -197,7 +200,7 @@ def main() -> int:
         "data": "synthetic (seeded PCG64 chunks; sizes and distributions of the five workloads)",
         "config": {
             "workload": "one step = C3 chain fp32 8,388,608 + C4 softmax bf16 32768x4096 + "
-                        "C5a softmax fp32 1024x131072 (online) + C5b tanh-GELU bf16 2^30",
+                        "C5a softmax fp32 1024x131072 (split across workgroups) + C5b tanh-GELU bf16 2^30",
             "step_bytes": step_bytes,
             "frac_of_peak": round(value / PEAK_HBM_GBS, 4),
             "kernels": kernels,
@@ -472,10 +475,22 @@ def cpu_baseline(host, kbytes):
         if dt >= CPU_BASELINE_MIN_SECONDS:
             break
     total = sum(kbytes.values()) * reps
+    # one core on a bounded sample: the first 2^24 elements of C5b and the
+    # first 4096 rows of C4 (4 bytes of algorithmic traffic per element each)
+    n1 = 1 << 24
+    t1 = time.perf_counter()
+    oracle.gelu_tanh(host["C5b"][:n1], threads=1)
+    g1 = n1 * 4 / (time.perf_counter() - t1) / 1e9
+    rows1 = host["C4"][:4096]
+    t1 = time.perf_counter()
+    oracle.softmax_rows(rows1, threads=1)
+    s1 = rows1.size * 4 / (time.perf_counter() - t1) / 1e9
     return {"value": round(total / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "seconds": round(dt, 3), "steps": reps,
             "sample": f"{reps} full steps (C3 + C4 + C5a + C5b, every element) through the "
-                      "double-precision C++ oracle, split over contiguous ranges/rows"}
+                      "double-precision C++ oracle, split over contiguous ranges/rows",
+            "single_core": {"C5b_first_2^24_GBps": round(g1, 3),
+                            "C4_first_4096_rows_GBps": round(s1, 3)}}
 
 
 def counters_run(fk, torch, launches, xs, ys):
