@@ -183,17 +183,18 @@ void attention_fwd_kernel(AttnArgs a) {
         // a causal block wholly above this wave's queries contributes nothing
         // (its last key block can be): the wave skips it (uniform branch)
         if (!(a.causal && kb0 > q0 + 31)) {
-            // S^T for the block's two 32-key tiles
-            f32x16 s[2];
+            // S^T for the block's two 32-key tiles; the tiles alternate so
+            // that consecutive MFMAs are independent (a lone tile is a chain
+            // of 8 dependent MFMAs, each also waiting on its LDS read)
+            f32x16 s[2] = {f32x16{}, f32x16{}};
+            const uint16_t* kbase = &Ks[buf][(lane % 32) * kKStride + g * 8];
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                s[t] = f32x16{};
-                const uint16_t* kbase = &Ks[buf][(t * 32 + lane % 32) * kKStride + g * 8];
+            for (int kk = 0; kk < kAttnD / 16; ++kk)
 #pragma unroll
-                for (int kk = 0; kk < kAttnD / 16; ++kk)
+                for (int t = 0; t < 2; ++t)
                     s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        *reinterpret_cast<const bf16x8*>(kbase + kk * 16), qf[kk], s[t], 0, 0, 0);
-            }
+                        *reinterpret_cast<const bf16x8*>(kbase + t * 32 * kKStride + kk * 16),
+                        qf[kk], s[t], 0, 0, 0);
 
             // mask (only blocks that reach past T or, causal, past the wave's
             // first query), then the block max over the query's 32 keys, in
@@ -252,12 +253,14 @@ void attention_fwd_kernel(AttnArgs a) {
             // O^T += V^T P^T; V^T fragment of d-tile dt, chunk (t, c): dims
             // dt * 32 + lane % 32, keys t * 32 + 16 c + 4 g + {0..3} and + 8,
             // read as two 8-byte runs (pairs of keys per 32-bit word)
+            // (key chunks outer, the four independent d-tiles inner)
+            const uint16_t* vbase = &Vt[buf][(lane % 32) * kVtStride + 4 * g];
 #pragma unroll
-            for (int dt = 0; dt < kAttnD / 32; ++dt) {
-                const uint16_t* vrow = &Vt[buf][(dt * 32 + lane % 32) * kVtStride + 4 * g];
+            for (int ch = 0; ch < 4; ++ch) {
+                const int k0 = (ch / 2) * 32 + (ch % 2) * 16;
 #pragma unroll
-                for (int ch = 0; ch < 4; ++ch) {
-                    const int k0 = (ch / 2) * 32 + (ch % 2) * 16;
+                for (int dt = 0; dt < kAttnD / 32; ++dt) {
+                    const uint16_t* vrow = vbase + dt * 32 * kVtStride;
                     const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + k0);
                     const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + k0 + 8);
                     const u32x4 w = {lo.x, lo.y, hi.x, hi.y};
