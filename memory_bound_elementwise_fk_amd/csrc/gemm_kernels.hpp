@@ -53,7 +53,7 @@ struct GemmShape {
 // Block index -> output tile (tm, tn). Blocks go to the 8 XCDs round-robin
 // (block b on XCD b % 8); when the block count divides by 8 the index is
 // first remapped so that each XCD works through a contiguous range of the
-// ordering below, then tiles are visited in column-strips of kGroup tile
+// ordering below, then tiles are visited in column-strips of kGemmGroup tile
 // rows, so the blocks in flight on one XCD share operand tiles in its L2.
 constexpr int kGemmGroup = 4;  // measured best of 4, 8, 16, 32 for 8192 x 16384 x 4096
 constexpr int kXcds = 8;
