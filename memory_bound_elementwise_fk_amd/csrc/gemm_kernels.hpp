@@ -14,11 +14,16 @@
 //
 // Block tile BM x BN, K step BK; the block's waves form a (BM/WM) x (BN/WN)
 // grid, each computing a WM x WN tile as (WM/32) x (WN/32) MFMA 32x32x16
-// tiles; the registers are budgeted for OCC waves per SIMD. Operand tiles are staged through LDS, double-buffered: the global
-// loads of step k+1 are in flight while step k is multiplied, and one
-// barrier per step separates the buffers. LDS rows are padded by 16 bytes
-// so the 16-byte fragment reads of 32 consecutive rows do not pile onto the
-// same banks.
+// tiles; the registers are budgeted for OCC waves per SIMD. Two main loops:
+//  * linear_gelu_kernel (any K that is a multiple of 8): operand tiles are
+//    staged through registers into LDS, double-buffered: the global loads of
+//    step k+1 are in flight while step k is multiplied, and one barrier per
+//    step separates the buffers. LDS rows are padded by 16 bytes so the
+//    16-byte fragment reads of 32 consecutive rows do not pile onto the
+//    same banks.
+//  * linear_gelu_dtl_kernel (K a multiple of 32): operands go straight from
+//    global memory into a ring of LDS stages (described at the kernel).
+// Both multiply in the same k order, so their outputs are bitwise equal.
 //
 // MFMA 32x32x16 bf16 operand layout (checked on the device): lane l supplies
 // A row l % 32 and B column l % 32, each at k = (l / 32) * 8 + e for its 8
