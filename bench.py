@@ -409,18 +409,35 @@ def measure_extras(fk, wl, torch, xs, ys, stream):
     del xl, wlin, bl, yl
 
     # FlashAttention forward on the pages' benchmark grid (B = 4, H = 32,
-    # d = 128), against torch's scaled_dot_product_attention
+    # d = 128, T = 128 ... 4096), against torch's scaled_dot_product_attention
     att = {}
-    for T in (1024, 4096):
+    for T in (128, 256, 512, 1024, 2048, 4096):
         qa, ka, va = (wl_.to_torch(wl_.draw(4 * 32 * T * 128, seed=6 + i, dtype="bf16"),
                                    "cuda:0").view(4, 32, T, 128) for i in range(3))
         oa = torch.empty_like(qa)
         for causal in (False, True):
             fl = 4.0 * 4 * 32 * T * T * 128 * (0.5 if causal else 1.0)
-            ms_fk = avg_ms(lambda: fk.fk_attention_fwd(qa, ka, va, oa, causal=causal), 5)
+            reps = 20 if T <= 1024 else 5
+            ms_fk = avg_ms(lambda: fk.fk_attention_fwd(qa, ka, va, oa, causal=causal), reps)
             ms_lib = avg_ms(lambda: torch.nn.functional.scaled_dot_product_attention(
-                qa, ka, va, is_causal=causal), 5)
+                qa, ka, va, is_causal=causal), reps)
             att[f"T{T}_{'causal' if causal else 'full'}"] = {
+                "ms": round(ms_fk, 4), "TFLOPs": round(fl / (ms_fk * 1e-3) / 1e12, 1),
+                "frac_of_mfma_peak": round(fl / (ms_fk * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "library_sdpa_ms": round(ms_lib, 4)}
+        del qa, ka, va, oa
+    # fp16, the dtype the pages benchmark
+    for T in (1024, 4096):
+        qa, ka, va = (wl_.to_torch(wl_.draw(4 * 32 * T * 128, seed=6 + i), "cuda:0")
+                      .to(torch.float16).view(4, 32, T, 128) for i in range(3))
+        oa = torch.empty_like(qa)
+        for causal in (False, True):
+            fl = 4.0 * 4 * 32 * T * T * 128 * (0.5 if causal else 1.0)
+            reps = 20 if T <= 1024 else 5
+            ms_fk = avg_ms(lambda: fk.fk_attention_fwd(qa, ka, va, oa, causal=causal), reps)
+            ms_lib = avg_ms(lambda: torch.nn.functional.scaled_dot_product_attention(
+                qa, ka, va, is_causal=causal), reps)
+            att[f"fp16_T{T}_{'causal' if causal else 'full'}"] = {
                 "ms": round(ms_fk, 4), "TFLOPs": round(fl / (ms_fk * 1e-3) / 1e12, 1),
                 "frac_of_mfma_peak": round(fl / (ms_fk * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                 "library_sdpa_ms": round(ms_lib, 4)}

@@ -16,8 +16,10 @@
  *   asynchronous, as the profiling notes on the pages stress: the host runs
  *   ahead of the device until it synchronises).
  * dtype: FK_F32 (IEEE binary32) or FK_BF16 (bfloat16, the upper half of a
- *   binary32). Input and output share the dtype. All arithmetic is fp32;
- *   bf16 outputs are rounded to nearest, ties to even; NaN stays NaN.
+ *   binary32); FK_F16 (IEEE binary16) for fk_attention_fwd only, every other
+ *   entry point returns FK_ERR_UNSUPPORTED for it. Input and output share
+ *   the dtype. All arithmetic is fp32; bf16 and fp16 outputs are rounded to
+ *   nearest, ties to even; NaN stays NaN.
  * Sizes: element counts and strides are in ELEMENTS (not bytes), int64_t.
  * Aliasing: y == x (exactly in place, and for row ops also ldy == ldx) is
  *   allowed: every element is read before the same lane writes it. Any
@@ -39,7 +41,7 @@
 extern "C" {
 #endif
 
-typedef enum { FK_F32 = 0, FK_BF16 = 1 } fk_dtype;
+typedef enum { FK_F32 = 0, FK_BF16 = 1, FK_F16 = 2 } fk_dtype;
 
 typedef enum {
     FK_OK = 0,
@@ -246,9 +248,10 @@ int fk_linear_gelu(const void* x, const void* w, const void* bias, void* y,
  * q, k, v, o: DEVICE tensors [B, H, T, d] of dtype addressed by strides
  * (host array of 12 element strides: batch, head and row stride of q, then
  * of k, v, o; the d values of a row are contiguous). fp32 statistics and
- * accumulators; P is rounded to bf16 before the P V product (as the page's
- * kernel rounds P to V's dtype); O rounded once to bf16.
- * Supported: dtype FK_BF16, d == 128, 16-byte aligned bases, strides that
+ * accumulators; P is rounded to the data dtype before the P V product (as
+ * the page's kernel rounds P to V's dtype); O rounded once to the dtype.
+ * Supported: dtype FK_BF16 or FK_F16 (the pages benchmark fp16), d == 128,
+ * 16-byte aligned bases, strides that
  * are multiples of 8, B * H * ceil(T / 128) <= 2^23 (one workgroup per 128
  * queries of one head) -- else FK_ERR_UNSUPPORTED. o must not
  * overlap q, k or v (FK_ERR_OVERLAP). B, H or T == 0: nothing to do.

@@ -18,6 +18,7 @@ LIB_PATH = Path(__file__).resolve().parent / "libfusedops.so"
 
 FK_F32 = 0
 FK_BF16 = 1
+FK_F16 = 2  # fk_attention_fwd only
 FK_OK = 0
 FK_ERR_INVALID_ARG = -1
 FK_ERR_UNSUPPORTED = -2
@@ -122,7 +123,9 @@ def _dtype_code(t) -> int:
         return FK_F32
     if t.dtype == torch.bfloat16:
         return FK_BF16
-    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+    if t.dtype == torch.float16:
+        return FK_F16  # the library refuses it outside attention
+    raise TypeError(f"unsupported dtype {t.dtype} (float32, bfloat16, or float16 for attention)")
 
 
 def _device_tensor(t, name: str):
@@ -237,7 +240,7 @@ def _dtype_arg(dtype) -> int:
     if isinstance(dtype, int):
         return dtype
     torch = _torch()
-    return FK_F32 if dtype == torch.float32 else FK_BF16 if dtype == torch.bfloat16 else -1
+    return {torch.float32: FK_F32, torch.bfloat16: FK_BF16, torch.float16: FK_F16}.get(dtype, -1)
 
 
 def fk_softmax_workspace_bytes(rows: int, cols: int, dtype) -> int:

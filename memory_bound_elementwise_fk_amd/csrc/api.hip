@@ -11,13 +11,18 @@ static_assert(FK_MAX_OPS == fk::kMaxOps, "op list size mismatch");
 static_assert(int(FK_OP_ADD_SCALAR) == int(fk::kOpAdd) && int(FK_OP_MUL_SCALAR) == int(fk::kOpMul) &&
                   int(FK_OP_GELU_TANH) == int(fk::kOpGelu),
               "op kind mismatch");
-static_assert(int(FK_F32) == int(fk::kF32) && int(FK_BF16) == int(fk::kBF16), "dtype mismatch");
+static_assert(int(FK_F32) == int(fk::kF32) && int(FK_BF16) == int(fk::kBF16) &&
+                  int(FK_F16) == int(fk::kF16),
+              "dtype mismatch");
 
 namespace {
 
 constexpr int64_t kI64Max = std::numeric_limits<int64_t>::max();
 
+// the dtypes of every entry point but attention (FK_F16 there is refused
+// as unsupported, any other value as invalid)
 bool dtype_ok(int dtype) { return dtype == FK_F32 || dtype == FK_BF16; }
+bool is_f16(int dtype) { return dtype == FK_F16; }
 int64_t esize(int dtype) { return dtype == FK_F32 ? 4 : 2; }
 
 // Byte ranges [a, a + na) and [b, b + nb) intersect.
@@ -47,6 +52,7 @@ int check_flat(const void* x, const void* y, int64_t n, int64_t elem_bytes, bool
 int check_rows(const void* x, const void* y, int64_t rows, int64_t cols, int64_t ldx,
                int64_t ldy, int dtype, bool* nothing_to_do) {
     *nothing_to_do = false;
+    if (is_f16(dtype)) return FK_ERR_UNSUPPORTED;
     if (!dtype_ok(dtype)) return FK_ERR_INVALID_ARG;
     if (rows < 0 || cols < 0) return FK_ERR_INVALID_ARG;
     if (rows == 0 || cols == 0) {
@@ -102,6 +108,7 @@ int softmax_self_managed(const void* x, void* y, int64_t rows, int64_t cols, int
 extern "C" {
 
 int fk_gelu_tanh(const void* x, void* y, int64_t n, int dtype, void* stream) {
+    if (is_f16(dtype)) return FK_ERR_UNSUPPORTED;
     if (!dtype_ok(dtype)) return FK_ERR_INVALID_ARG;
     bool skip = false;
     const int st = check_flat(x, y, n, esize(dtype), &skip);
@@ -112,6 +119,7 @@ int fk_gelu_tanh(const void* x, void* y, int64_t n, int dtype, void* stream) {
 
 int fk_elementwise_chain(const void* x, void* y, int64_t n, int dtype, const fk_op* ops,
                          int n_ops, void* stream) {
+    if (is_f16(dtype)) return FK_ERR_UNSUPPORTED;
     if (!dtype_ok(dtype)) return FK_ERR_INVALID_ARG;
     if (ops == nullptr || n_ops < 1 || n_ops > FK_MAX_OPS) return FK_ERR_INVALID_ARG;
     fk::OpList list{};
@@ -160,6 +168,7 @@ int fk_softmax_rows_ws(const void* x, void* y, int64_t rows, int64_t cols, int64
 }
 
 int64_t fk_softmax_workspace_bytes(int64_t rows, int64_t cols, int dtype) {
+    if (is_f16(dtype)) return FK_ERR_UNSUPPORTED;
     if (!dtype_ok(dtype) || rows < 0 || cols < 0) return FK_ERR_INVALID_ARG;
     if (rows == 0 || cols == 0) return 0;
     return fk::softmax_workspace_bytes(rows, cols, static_cast<fk::Dtype>(dtype));
@@ -201,6 +210,7 @@ int fk_layernorm_rows(const void* x, void* y, int64_t rows, int64_t cols, int64_
 
 int fk_gelu_tanh_backward(const void* x, const void* dy, void* dx, int64_t n, int dtype,
                           void* stream) {
+    if (is_f16(dtype)) return FK_ERR_UNSUPPORTED;
     if (!dtype_ok(dtype)) return FK_ERR_INVALID_ARG;
     bool skip = false;
     int st = check_flat(x, dx, n, esize(dtype), &skip);  // also: dx == x or disjoint
@@ -226,6 +236,7 @@ int fk_softmax_rows_backward(const void* y, const void* dy, void* dx, int64_t ro
 }
 
 int64_t fk_softmax_backward_max_cols(int dtype) {
+    if (is_f16(dtype)) return FK_ERR_UNSUPPORTED;
     if (!dtype_ok(dtype)) return FK_ERR_INVALID_ARG;
     return fk::softmax_backward_max_cols(static_cast<fk::Dtype>(dtype));
 }
@@ -233,6 +244,7 @@ int64_t fk_softmax_backward_max_cols(int dtype) {
 int fk_linear_gelu(const void* x, const void* w, const void* bias, void* y, int64_t M, int64_t N,
                    int64_t K, int64_t ldx, int64_t ldw, int64_t ldy, int fuse_gelu, int dtype,
                    void* stream) {
+    if (is_f16(dtype)) return FK_ERR_UNSUPPORTED;
     if (!dtype_ok(dtype)) return FK_ERR_INVALID_ARG;
     if (M < 0 || N < 0 || K < 0) return FK_ERR_INVALID_ARG;
     if (fuse_gelu != 0 && fuse_gelu != 1) return FK_ERR_INVALID_ARG;
@@ -260,7 +272,8 @@ int fk_linear_gelu(const void* x, const void* w, const void* bias, void* y, int6
 int fk_attention_fwd(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H,
                      int64_t T, int64_t d, const int64_t* strides, int causal, int dtype,
                      void* stream) {
-    if (!dtype_ok(dtype) || B < 0 || H < 0 || T < 0 || d < 1) return FK_ERR_INVALID_ARG;
+    if ((!dtype_ok(dtype) && !is_f16(dtype)) || B < 0 || H < 0 || T < 0 || d < 1)
+        return FK_ERR_INVALID_ARG;
     if (causal != 0 && causal != 1) return FK_ERR_INVALID_ARG;
     if (strides == nullptr) return FK_ERR_INVALID_ARG;
     if (B == 0 || H == 0 || T == 0) return FK_OK;
@@ -269,7 +282,7 @@ int fk_attention_fwd(const void* q, const void* k, const void* v, void* o, int64
         if (strides[i] < 0) return FK_ERR_INVALID_ARG;
     for (int t = 0; t < 4; ++t)
         if (strides[3 * t + 2] < d) return FK_ERR_INVALID_ARG;  // rows of d contiguous values
-    if (dtype != FK_BF16 || d != fk::attention_head_dim()) return FK_ERR_UNSUPPORTED;
+    if (dtype == FK_F32 || d != fk::attention_head_dim()) return FK_ERR_UNSUPPORTED;
     const uintptr_t addr = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
                            reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o);
     if ((addr & 15u) != 0) return FK_ERR_UNSUPPORTED;
@@ -292,15 +305,18 @@ int fk_attention_fwd(const void* q, const void* k, const void* v, void* o, int64
         ranges_overlap(o, ext[3], v, ext[2]))
         return FK_ERR_OVERLAP;
     return hip_status(fk::launch_attention_fwd(q, k, v, o, B, H, T, strides, causal,
+                                               static_cast<fk::Dtype>(dtype),
                                                static_cast<hipStream_t>(stream)));
 }
 
 int64_t fk_layernorm_max_cols(int dtype) {
+    if (is_f16(dtype)) return FK_ERR_UNSUPPORTED;
     if (!dtype_ok(dtype)) return FK_ERR_INVALID_ARG;
     return fk::layernorm_max_cols(static_cast<fk::Dtype>(dtype));
 }
 
 int64_t fk_softmax_onchip_max_cols(int dtype) {
+    if (is_f16(dtype)) return FK_ERR_UNSUPPORTED;
     if (!dtype_ok(dtype)) return FK_ERR_INVALID_ARG;
     return fk::softmax_onchip_max_cols(static_cast<fk::Dtype>(dtype));
 }

@@ -15,7 +15,7 @@ int64_t attention_workgroups(int64_t B, int64_t H, int64_t T) {
 
 hipError_t launch_attention_fwd(const void* q, const void* k, const void* v, void* o, int64_t B,
                                 int64_t H, int64_t T, const int64_t* strides, int causal,
-                                hipStream_t s) {
+                                Dtype dt, hipStream_t s) {
     AttnArgs a;
     a.q = static_cast<const uint16_t*>(q);
     a.k = static_cast<const uint16_t*>(k);
@@ -32,8 +32,9 @@ hipError_t launch_attention_fwd(const void* q, const void* k, const void* v, voi
     a.causal = causal;
     const int64_t nwg = attention_workgroups(B, H, T);  // <= 2^23, checked by the caller
     void* args[] = {&a};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&attention_fwd_kernel),
-                           dim3(static_cast<unsigned>(nwg)), dim3(kAttnThreads), args, 0, s);
+    const void* fn = dt == kF16 ? reinterpret_cast<const void*>(&attention_fwd_kernel<AttnF16>)
+                                : reinterpret_cast<const void*>(&attention_fwd_kernel<AttnBF16>);
+    return hipLaunchKernel(fn, dim3(static_cast<unsigned>(nwg)), dim3(kAttnThreads), args, 0, s);
 }
 
 }  // namespace fk

@@ -1,5 +1,5 @@
-// attention_kernels.hpp -- FlashAttention forward for gfx950 (bf16 in and
-// out, fp32 statistics and accumulators, head dimension 128).
+// attention_kernels.hpp -- FlashAttention forward for gfx950 (bf16 or fp16
+// in and out, fp32 statistics and accumulators, head dimension 128).
 //
 // O = softmax(Q K^T / sqrt(d) + mask) V, computed tile by tile without
 // materialising the T x T scores ("Lecture 6: GPU Kernels and Triton",
@@ -60,13 +60,38 @@ struct AttnArgs {
 };
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// The 16-bit element types the kernel takes: the MFMA operand vector, the
+// 32x32x16 MFMA with fp32 accumulation, and fp32 -> two packed elements
+// rounded to nearest even.
+struct AttnBF16 {
+    typedef bf16x8 frag;
+    __device__ static inline f32x16 mfma(frag a, frag b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    __device__ static inline uint32_t cvt2(float a, float b) { return IoBF16::cvt2(a, b); }
+};
+struct AttnF16 {
+    typedef f16x8 frag;
+    __device__ static inline f32x16 mfma(frag a, frag b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    __device__ static inline uint32_t cvt2(float a, float b) {
+        f32x2 f = {a, b};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+    }
+};
 
 // Two waves per SIMD (two workgroups per CU; LDS 70 KiB each): with one, a
 // wave's MFMA, exponential and LDS phases run back to back and the K/V loads
 // barely overlap them; the second workgroup fills those gaps. The compiler
 // fits the kernel in 256 registers (no AGPRs, no spills) when asked to.
+template <class EL>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attention_fwd_kernel(AttnArgs a) {
+    typedef typename EL::frag frag;
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kAttnBC * kKStride];
     __shared__ __attribute__((aligned(16))) uint16_t Vt[2][kAttnD * kVtStride];
 
@@ -97,12 +122,12 @@ void attention_fwd_kernel(AttnArgs a) {
     const int64_t myq = q0 + lane % 32;  // the query of this lane
 
     // Q^T fragments (B operand): query myq, dims kk * 16 + g * 8 + e
-    bf16x8 qf[kAttnD / 16];
+    frag qf[kAttnD / 16];
 #pragma unroll
     for (int kk = 0; kk < kAttnD / 16; ++kk) {
         u32x4 w = {0u, 0u, 0u, 0u};
         if (myq < a.T) w = *reinterpret_cast<const u32x4*>(Q + myq * a.qt + kk * 16 + g * 8);
-        qf[kk] = __builtin_bit_cast(bf16x8, w);
+        qf[kk] = __builtin_bit_cast(frag, w);
     }
 
     // key blocks to visit: all, or up to the block's last query when causal
@@ -192,9 +217,9 @@ void attention_fwd_kernel(AttnArgs a) {
             for (int kk = 0; kk < kAttnD / 16; ++kk)
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
-                    s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        *reinterpret_cast<const bf16x8*>(kbase + t * 32 * kKStride + kk * 16),
-                        qf[kk], s[t], 0, 0, 0);
+                    s[t] = EL::mfma(
+                        *reinterpret_cast<const frag*>(kbase + t * 32 * kKStride + kk * 16),
+                        qf[kk], s[t]);
 
             // mask (only blocks that reach past T or, causal, past the wave's
             // first query), then the block max over the query's 32 keys, in
@@ -220,7 +245,7 @@ void attention_fwd_kernel(AttnArgs a) {
             const float base = mn == -__builtin_inff() ? 0.0f : mn;
             const float corr = (m == mn) ? 1.0f : exp2_raw(m - base);
             float bs = 0.0f;
-            bf16x8 pf[4];  // P^T fragments: chunk 2 t + c of tile t
+            frag pf[4];  // P^T fragments: chunk 2 t + c of tile t
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
 #pragma unroll
@@ -233,11 +258,11 @@ void attention_fwd_kernel(AttnArgs a) {
                         bs += pv[e];
                     }
                     u32x4 w;
-                    w.x = IoBF16::cvt2(pv[0], pv[1]);
-                    w.y = IoBF16::cvt2(pv[2], pv[3]);
-                    w.z = IoBF16::cvt2(pv[4], pv[5]);
-                    w.w = IoBF16::cvt2(pv[6], pv[7]);
-                    pf[t * 2 + c] = __builtin_bit_cast(bf16x8, w);
+                    w.x = EL::cvt2(pv[0], pv[1]);
+                    w.y = EL::cvt2(pv[2], pv[3]);
+                    w.z = EL::cvt2(pv[4], pv[5]);
+                    w.w = EL::cvt2(pv[6], pv[7]);
+                    pf[t * 2 + c] = __builtin_bit_cast(frag, w);
                 }
             }
             bs += __shfl_xor(bs, 32);
@@ -264,8 +289,7 @@ void attention_fwd_kernel(AttnArgs a) {
                     const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + k0);
                     const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + k0 + 8);
                     const u32x4 w = {lo.x, lo.y, hi.x, hi.y};
-                    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8, w), pf[ch], acc[dt], 0, 0, 0);
+                    acc[dt] = EL::mfma(__builtin_bit_cast(frag, w), pf[ch], acc[dt]);
                 }
             }
         }
@@ -283,8 +307,8 @@ void attention_fwd_kernel(AttnArgs a) {
 #pragma unroll
             for (int v4 = 0; v4 < 4; ++v4) {
                 const int d = dt * 32 + v4 * 8 + g * 4;
-                uint32_t w0 = IoBF16::cvt2(acc[dt][v4 * 4 + 0] * r, acc[dt][v4 * 4 + 1] * r);
-                uint32_t w1 = IoBF16::cvt2(acc[dt][v4 * 4 + 2] * r, acc[dt][v4 * 4 + 3] * r);
+                uint32_t w0 = EL::cvt2(acc[dt][v4 * 4 + 0] * r, acc[dt][v4 * 4 + 1] * r);
+                uint32_t w1 = EL::cvt2(acc[dt][v4 * 4 + 2] * r, acc[dt][v4 * 4 + 3] * r);
                 *reinterpret_cast<uint64_t*>(orow + d) = uint64_t(w0) | (uint64_t(w1) << 32);
             }
         }

@@ -11,7 +11,7 @@ namespace fk {
 constexpr int kMaxOps = 8;  // equals FK_MAX_OPS of the public header
 
 enum OpKind : int32_t { kOpAdd = 1, kOpMul = 2, kOpGelu = 3 };
-enum Dtype : int { kF32 = 0, kBF16 = 1 };
+enum Dtype : int { kF32 = 0, kBF16 = 1, kF16 = 2 };  // kF16: attention only
 
 // Op list copied by value into the kernel arguments (no device copy).
 struct OpList {
@@ -67,10 +67,10 @@ hipError_t launch_linear_gelu(const void* x, const void* w, const void* bias, vo
 int64_t linear_tiles(int64_t M, int64_t N);
 int64_t linear_max_tiles();
 
-// FlashAttention forward, bf16, head dimension attention_head_dim();
+// FlashAttention forward, bf16 or fp16, head dimension attention_head_dim();
 // strides[12] = (batch, head, row) strides of q, k, v, o in elements.
 hipError_t launch_attention_fwd(const void* q, const void* k, const void* v, void* o, int64_t B,
-                                int64_t H, int64_t T, const int64_t* strides, int causal,
+                                int64_t H, int64_t T, const int64_t* strides, int causal, Dtype dt,
                                 hipStream_t s);
 int64_t attention_head_dim();
 // workgroups of one launch: ceil(T / 128) * B * H (caller keeps it <= 2^23

@@ -314,12 +314,13 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool = True,
               rows: dict | None = None) -> np.ndarray:
     """O = softmax(Q K^T / sqrt(d) + mask) V per (batch, head), rounded once.
 
-    q, k, v: [B, H, T, d] (float32, or bf16 as uint16 bits). The causal mask
-    keeps key j for query i when j <= i ("Lecture 6: GPU Kernels and Triton",
-    section 8: the mask q_offset >= kv_offset). Scores and the products use
-    numpy's float64 matmul (a library step); the row softmax is the oracle's
-    own (max, exponentials, sum, normalise, in double); the result is
-    rounded to fp32 and, for bf16 data, then to bf16. ``rows`` maps (b, h)
+    q, k, v: [B, H, T, d] (float32, float16, or bf16 as uint16 bits). The
+    causal mask keeps key j for query i when j <= i ("Lecture 6: GPU Kernels
+    and Triton", section 8: the mask q_offset >= kv_offset). Scores and the
+    products use numpy's float64 matmul (a library step); the row softmax is
+    the oracle's own (max, exponentials, sum, normalise, in double); the
+    result is rounded to fp32 and, for bf16 or fp16 data, then to that type
+    (nearest even). ``rows`` maps (b, h)
     to an array of query indices to compute only those rows (sampling);
     then the result is {(b, h): [len(rows), d]}.
     """
@@ -335,7 +336,9 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool = True,
             sc = np.where(np.arange(T)[None, :] <= np.asarray(qi)[:, None], sc, -np.inf)
         pr = softmax_rows(np.ascontiguousarray(sc))
         o = (pr @ vd).astype(np.float32)
-        return f32_to_bf16(o).reshape(o.shape) if q.dtype == np.uint16 else o
+        if q.dtype == np.uint16:
+            return f32_to_bf16(o).reshape(o.shape)
+        return o.astype(np.float16) if q.dtype == np.float16 else o
 
     if rows is not None:
         return {key: one(key[0], key[1], np.asarray(idx)) for key, idx in rows.items()}

@@ -72,7 +72,7 @@ def test_gelu_validation(L, dtype):
     assert g(None, B, 5, dtype, None) == fk.FK_ERR_INVALID_ARG
     assert g(A, None, 5, dtype, None) == fk.FK_ERR_INVALID_ARG
     assert g(A, B, -1, dtype, None) == fk.FK_ERR_INVALID_ARG
-    assert g(A, B, 5, 2, None) == fk.FK_ERR_INVALID_ARG
+    assert g(A, B, 5, 3, None) == fk.FK_ERR_INVALID_ARG
     assert g(A, B, 5, -1, None) == fk.FK_ERR_INVALID_ARG
     assert g(A, A + 4, 5, dtype, None) == fk.FK_ERR_OVERLAP   # partial overlap
     assert g(A + 8, A, 5, dtype, None) == fk.FK_ERR_OVERLAP
@@ -260,6 +260,33 @@ def test_attention_validation(L):
     assert f(A, B, C, D, 3000, 3000, 16, 128, good, 1, bf, None) == fk.FK_ERR_UNSUPPORTED
     assert f(A, B, C, D, 64, 1024, 128 * 129, 128, good, 1, bf, None) == fk.FK_ERR_UNSUPPORTED
     assert f(A, B, C, D, 1, 1, 1 << 31, 128, good, 1, bf, None) == fk.FK_ERR_UNSUPPORTED
+
+
+def test_fp16_is_for_attention_only(L):
+    import ctypes
+    f16 = fk.FK_F16
+    C, D = 0x7F0000C00000, 0x7F0000E00000
+    U = fk.FK_ERR_UNSUPPORTED
+    assert L.fk_gelu_tanh(A, B, 5, f16, None) == U
+    assert L.fk_elementwise_chain(A, B, 10, f16, _ops((1, 1.0)), 1, None) == U
+    for name in ("fk_softmax_rows", "fk_softmax_rows_online"):
+        assert getattr(L, name)(A, B, 4, 10, 10, 10, f16, None) == U
+    assert L.fk_softmax_rows_ws(A, B, 4, 10, 10, 10, f16, C, 64, None) == U
+    assert L.fk_softmax_workspace_bytes(4, 10, f16) == U
+    assert L.fk_softmax_onchip_max_cols(f16) == U
+    assert L.fk_layernorm_rows(A, B, 4, 10, 10, 10, None, None, 1e-5, 0, f16, None) == U
+    assert L.fk_layernorm_max_cols(f16) == U
+    assert L.fk_gelu_tanh_backward(A, B, C, 5, f16, None) == U
+    assert L.fk_softmax_rows_backward(A, B, C, 4, 10, 10, 10, 10, f16, None) == U
+    assert L.fk_softmax_backward_max_cols(f16) == U
+    assert L.fk_linear_gelu(A, B, None, C, 4, 10, 16, 16, 16, 10, 1, f16, None) == U
+    # attention takes it: the same validation as bf16
+    st = (ctypes.c_int64 * 12)(*([2 * 3 * 128, 3 * 128, 128] * 4))
+    a = L.fk_attention_fwd
+    assert a(A, B, C, D, 0, 3, 16, 128, st, 1, f16, None) == fk.FK_OK
+    assert a(A, B, C, D, 2, 3, 16, 64, st, 1, f16, None) == U            # d != 128
+    assert a(A, B, C, A + 256, 2, 3, 16, 128, st, 1, f16, None) == fk.FK_ERR_OVERLAP
+    assert a(A, B, C, D, 2, 3, 16, 128, st, 1, 3, None) == fk.FK_ERR_INVALID_ARG
 
 
 def test_copy_validation(L):

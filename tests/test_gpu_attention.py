@@ -9,6 +9,8 @@ the P V product (as the page's kernel rounds P to V's dtype): relative error
 l uses the unrounded p); the fp32 scores (128 bf16 products) move the
 weights by ~1e-4 relative, far below that; the output rounding to bf16 adds
 half an ulp on each side. 2^-8 leaves a factor 2 over the P rounding.
+fp16 data (the pages benchmark fp16): the same argument with P rounded to
+fp16 (2^-11 relative): |o - r| <= ulp_fp16(|r|) + 2^-10 max|v|.
 """
 import numpy as np
 import pytest
@@ -27,22 +29,34 @@ def bf16_ulp(r):
     return np.exp2(e - 7)
 
 
-def qkv(B, H, T, seed, d=128):
+def fp16_ulp(r):
+    e = np.floor(np.log2(np.maximum(np.abs(r), 2.0 ** -14)))
+    return np.exp2(e - 10)
+
+
+def f64(a):
+    """bf16 bits (uint16) or float16/float32 values -> float64."""
+    return oracle.bf16_to_f32(a).astype(np.float64) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
+def qkv(B, H, T, seed, d=128, dt="bf16"):
     rng = np.random.default_rng(seed)
     out = []
     for _ in range(3):
         a = rng.standard_normal((B, H, T, d)).astype(np.float32)
-        out.append(wl.f32_to_bf16_bits(a).reshape(B, H, T, d))
+        out.append(a.astype(np.float16) if dt == "fp16"
+                   else wl.f32_to_bf16_bits(a).reshape(B, H, T, d))
     return out
 
 
 def check_rows(got_rows, ref_rows, v, what):
-    """got_rows / ref_rows: {(b, h): [n, d] bf16}."""
+    """got_rows / ref_rows: {(b, h): [n, d]} of v's storage type."""
+    fp16 = v.dtype == np.float16
     for key, ref in ref_rows.items():
-        g = oracle.bf16_to_f32(got_rows[key]).astype(np.float64)
-        r = oracle.bf16_to_f32(ref).astype(np.float64)
-        vmax = float(np.abs(oracle.bf16_to_f32(v[key[0], key[1]])).max())
-        lim = bf16_ulp(r) + 2.0 ** -8 * vmax
+        g = f64(got_rows[key])
+        r = f64(ref)
+        vmax = float(np.abs(f64(v[key[0], key[1]])).max())
+        lim = (fp16_ulp(r) + 2.0 ** -10 * vmax) if fp16 else (bf16_ulp(r) + 2.0 ** -8 * vmax)
         err = np.abs(g - r)
         bad = np.flatnonzero(err > lim)
         assert bad.size == 0, f"{what} {key}: {bad.size} beyond tolerance, worst excess {(err - lim).max():.3e}"
@@ -56,8 +70,9 @@ def run(q, k, v, causal):
 @pytest.mark.parametrize("B,H,T", [(1, 1, 1), (1, 2, 33), (2, 3, 128), (1, 2, 200), (1, 1, 513),
                                    (2, 2, 1000)])
 @pytest.mark.parametrize("causal", [True, False])
-def test_attention_shapes(B, H, T, causal):
-    q, k, v = qkv(B, H, T, seed=B * 100 + H * 10 + T)
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
+def test_attention_shapes(B, H, T, causal, dt):
+    q, k, v = qkv(B, H, T, seed=B * 100 + H * 10 + T, dt=dt)
     got = run(q, k, v, causal)
     ref = oracle.attention(q, k, v, causal=causal)
     rows = {(b, h): np.arange(T) for b in range(B) for h in range(H)}
@@ -83,10 +98,11 @@ def test_attention_strided_bthd_layout():
 
 
 @pytest.mark.parametrize("T", [128, 1024, 4096])
-def test_attention_benchmark_grid_sampled(T):
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
+def test_attention_benchmark_grid_sampled(T, dt):
     # the pages' benchmark grid: B = 4, H = 32, d = 128
     B, H = 4, 32
-    q, k, v = qkv(B, H, T, seed=T)
+    q, k, v = qkv(B, H, T, seed=T, dt=dt)
     for causal in (True, False):
         o = fk.attention_fwd(to_dev(q), to_dev(k), to_dev(v), causal=causal)
         rng = np.random.default_rng(T + causal)
@@ -95,7 +111,7 @@ def test_attention_benchmark_grid_sampled(T):
         ref = oracle.attention(q, k, v, causal=causal, rows=picks)
         got = {key: to_host(o[key[0], key[1]][torch.from_numpy(idx).to(DEV)])
                for key, idx in picks.items()}
-        check_rows(got, ref, v, f"T={T} causal={causal}")
+        check_rows(got, ref, v, f"{dt} T={T} causal={causal}")
 
 
 def test_attention_closed_forms():
@@ -111,8 +127,27 @@ def test_attention_closed_forms():
     assert np.array_equal(run(*qkv(1, 2, 77, seed=4), True)[:, :, 0], qkv(1, 2, 77, seed=4)[2][:, :, 0])
 
 
-def test_attention_bitwise_reproducible():
-    q, k, v = (to_dev(a) for a in qkv(2, 4, 700, seed=5))
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
+def test_attention_bitwise_reproducible(dt):
+    q, k, v = (to_dev(a) for a in qkv(2, 4, 700, seed=5, dt=dt))
     a = fk.attention_fwd(q, k, v)
     b = fk.attention_fwd(q, k, v)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_attention_fp16_strided_and_closed_form():
+    B, H, T, d = 2, 4, 300, 128
+    rng = np.random.default_rng(17)
+    base = [rng.standard_normal((B, T, H, d)).astype(np.float16) for _ in range(3)]
+    qt, kt, vt = (to_dev(a).permute(0, 2, 1, 3) for a in base)
+    ot = torch.empty((B, T, H, d), dtype=torch.float16, device=DEV).permute(0, 2, 1, 3)
+    fk.fk_attention_fwd(qt, kt, vt, ot, causal=False)
+    got = to_host(ot.contiguous())
+    q, k, v = (np.ascontiguousarray(a.transpose(0, 2, 1, 3)) for a in base)
+    ref = oracle.attention(q, k, v, causal=False)
+    rows = {(b, h): np.arange(T) for b in range(B) for h in range(H)}
+    check_rows({key: got[key[0], key[1]] for key in rows},
+               {key: ref[key[0], key[1]] for key in rows}, v, "fp16 B,T,H,d layout")
+    # row 0 under the causal mask is V[0] exactly
+    q, k, v = qkv(1, 2, 77, seed=4, dt="fp16")
+    assert np.array_equal(run(q, k, v, True)[:, :, 0], v[:, :, 0])

@@ -7,7 +7,8 @@ Pinned against torch's scaled_dot_product_attention in float64, and by
 cases with closed forms: Q = 0 gives uniform weights (O = mean of the
 allowed V rows: the prefix mean under the causal mask), one dominant score
 selects its V row, T = 1 and the first causal row give V[0], and without
-the mask a joint permutation of K and V leaves O unchanged.
+the mask a joint permutation of K and V leaves O unchanged. bf16 and fp16
+data are the double result rounded to fp32 and then to the storage type.
 """
 import numpy as np
 import torch
@@ -80,3 +81,20 @@ def test_bf16_rounding_and_sampled_rows():
     assert full.dtype == np.uint16
     part = oracle.attention(q, k, v, rows={(0, 1): np.array([0, 7, 32])})
     assert np.array_equal(part[(0, 1)], full[0, 1][[0, 7, 32]])
+
+
+def test_fp16_data_round_the_double_result_twice():
+    """fp16 inputs: the double result rounded to fp32, then to fp16 (nearest
+    even, numpy's conversion), pinned against torch SDPA in float64 on the
+    same fp16 values; within one fp16 ulp of the double result."""
+    q, k, v = (RNG.standard_normal((1, 2, 40, 32)).astype(np.float16) for _ in range(3))
+    for causal in (True, False):
+        got = oracle.attention(q, k, v, causal=causal)
+        assert got.dtype == np.float16
+        ref = F.scaled_dot_product_attention(
+            *(torch.from_numpy(a.astype(np.float64)) for a in (q, k, v)), is_causal=causal).numpy()
+        assert np.array_equal(got, ref.astype(np.float32).astype(np.float16))
+        ulp = np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64)
+        assert np.all(np.abs(got.astype(np.float64) - ref) <= ulp)
+    part = oracle.attention(q, k, v, rows={(0, 1): np.array([0, 39])})
+    assert np.array_equal(part[(0, 1)], oracle.attention(q, k, v)[0, 1][[0, 39]])
