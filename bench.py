@@ -406,7 +406,16 @@ def measure_extras(fk, wl, torch, xs, ys, stream):
         "library_linear_ms": round(lib_mm, 4),
         "library_linear_then_gelu_ms": round(lib_unfused, 4),
         "note": "library = torch.nn.functional.linear (hipBLASLt) and its separate GELU"}
-    del xl, wlin, bl, yl
+    # the same in fp16
+    xh, wh, bh = xl.to(torch.float16), wlin.to(torch.float16), bl.to(torch.float16)
+    yh = torch.empty((M, N), dtype=torch.float16, device="cuda:0")
+    fused16 = avg_ms(lambda: fk.fk_linear_gelu(xh, wh, bh, yh), 10)
+    lib16 = avg_ms(lambda: torch.nn.functional.gelu(torch.nn.functional.linear(xh, wh, bh),
+                                                    approximate="tanh"), 10)
+    out["linear_gelu"]["fp16"] = {"fused_ms": round(fused16, 4),
+                                  "fused_TFLOPs": round(flops / (fused16 * 1e-3) / 1e12, 1),
+                                  "library_linear_then_gelu_ms": round(lib16, 4)}
+    del xl, wlin, bl, yl, xh, wh, bh, yh
 
     # FlashAttention forward on the pages' benchmark grid (B = 4, H = 32,
     # d = 128, T = 128 ... 4096), against torch's scaled_dot_product_attention

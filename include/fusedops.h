@@ -16,8 +16,8 @@
  *   asynchronous, as the profiling notes on the pages stress: the host runs
  *   ahead of the device until it synchronises).
  * dtype: FK_F32 (IEEE binary32) or FK_BF16 (bfloat16, the upper half of a
- *   binary32); FK_F16 (IEEE binary16) for fk_attention_fwd only, every other
- *   entry point returns FK_ERR_UNSUPPORTED for it. Input and output share
+ *   binary32); FK_F16 (IEEE binary16) for fk_linear_gelu and fk_attention_fwd
+ *   only, every other entry point returns FK_ERR_UNSUPPORTED for it. Input and output share
  *   the dtype. All arithmetic is fp32; bf16 and fp16 outputs are rounded to
  *   nearest, ties to even; NaN stays NaN.
  * Sizes: element counts and strides are in ELEMENTS (not bytes), int64_t.
@@ -228,8 +228,8 @@ int64_t fk_softmax_backward_max_cols(int dtype);
  * of a second pass over the M x N product. x: M rows of K (row stride ldx),
  * w: N rows of K (a Linear weight, row stride ldw), bias: N values or NULL,
  * y: M rows of N (row stride ldy); all DEVICE memory of dtype. fp32
- * accumulation; y rounded once to bf16 (nearest even).
- * Supported: dtype FK_BF16 only; K, ldx and ldw multiples of 8; x and w
+ * accumulation; y rounded once to the dtype (nearest even).
+ * Supported: dtype FK_BF16 or FK_F16; K, ldx and ldw multiples of 8; x and w
  * 16-byte aligned -- else FK_ERR_UNSUPPORTED. y must not overlap x, w or
  * bias (FK_ERR_OVERLAP). M == 0 or N == 0: nothing to do. K == 0 gives
  * GELU(bias).

@@ -18,7 +18,7 @@ LIB_PATH = Path(__file__).resolve().parent / "libfusedops.so"
 
 FK_F32 = 0
 FK_BF16 = 1
-FK_F16 = 2  # fk_attention_fwd only
+FK_F16 = 2  # fk_linear_gelu and fk_attention_fwd only
 FK_OK = 0
 FK_ERR_INVALID_ARG = -1
 FK_ERR_UNSUPPORTED = -2
@@ -124,8 +124,8 @@ def _dtype_code(t) -> int:
     if t.dtype == torch.bfloat16:
         return FK_BF16
     if t.dtype == torch.float16:
-        return FK_F16  # the library refuses it outside attention
-    raise TypeError(f"unsupported dtype {t.dtype} (float32, bfloat16, or float16 for attention)")
+        return FK_F16  # the library refuses it outside Linear and attention
+    raise TypeError(f"unsupported dtype {t.dtype} (float32, bfloat16, or float16 for Linear and attention)")
 
 
 def _device_tensor(t, name: str):

@@ -19,8 +19,8 @@ namespace {
 
 constexpr int64_t kI64Max = std::numeric_limits<int64_t>::max();
 
-// the dtypes of every entry point but attention (FK_F16 there is refused
-// as unsupported, any other value as invalid)
+// the dtypes of every entry point but Linear and attention (FK_F16 there is
+// refused as unsupported, any other value as invalid)
 bool dtype_ok(int dtype) { return dtype == FK_F32 || dtype == FK_BF16; }
 bool is_f16(int dtype) { return dtype == FK_F16; }
 int64_t esize(int dtype) { return dtype == FK_F32 ? 4 : 2; }
@@ -244,14 +244,13 @@ int64_t fk_softmax_backward_max_cols(int dtype) {
 int fk_linear_gelu(const void* x, const void* w, const void* bias, void* y, int64_t M, int64_t N,
                    int64_t K, int64_t ldx, int64_t ldw, int64_t ldy, int fuse_gelu, int dtype,
                    void* stream) {
-    if (is_f16(dtype)) return FK_ERR_UNSUPPORTED;
-    if (!dtype_ok(dtype)) return FK_ERR_INVALID_ARG;
+    if (!dtype_ok(dtype) && !is_f16(dtype)) return FK_ERR_INVALID_ARG;
     if (M < 0 || N < 0 || K < 0) return FK_ERR_INVALID_ARG;
     if (fuse_gelu != 0 && fuse_gelu != 1) return FK_ERR_INVALID_ARG;
     if (M == 0 || N == 0) return FK_OK;
     if (y == nullptr || (K > 0 && (x == nullptr || w == nullptr))) return FK_ERR_INVALID_ARG;
     if (ldy < N || (K > 0 && (ldx < K || ldw < K))) return FK_ERR_INVALID_ARG;
-    if (dtype != FK_BF16) return FK_ERR_UNSUPPORTED;
+    if (dtype == FK_F32) return FK_ERR_UNSUPPORTED;
     // x and w are read only when K > 0 (K == 0 gives GELU(bias))
     if (K > 0 && (K % 8 != 0 || ldx % 8 != 0 || ldw % 8 != 0 ||
                   ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w)) & 15u) != 0))
@@ -266,6 +265,7 @@ int fk_linear_gelu(const void* x, const void* w, const void* bias, void* y, int6
         return FK_ERR_OVERLAP;
     if (bias != nullptr && ranges_overlap(y, by, bias, N * 2)) return FK_ERR_OVERLAP;
     return hip_status(fk::launch_linear_gelu(x, w, bias, y, M, N, K, ldx, ldw, ldy, fuse_gelu,
+                                             static_cast<fk::Dtype>(dtype),
                                              static_cast<hipStream_t>(stream)));
 }
 

@@ -32,8 +32,8 @@ hipError_t launch_attention_fwd(const void* q, const void* k, const void* v, voi
     a.causal = causal;
     const int64_t nwg = attention_workgroups(B, H, T);  // <= 2^23, checked by the caller
     void* args[] = {&a};
-    const void* fn = dt == kF16 ? reinterpret_cast<const void*>(&attention_fwd_kernel<AttnF16>)
-                                : reinterpret_cast<const void*>(&attention_fwd_kernel<AttnBF16>);
+    const void* fn = dt == kF16 ? reinterpret_cast<const void*>(&attention_fwd_kernel<MmaF16>)
+                                : reinterpret_cast<const void*>(&attention_fwd_kernel<MmaBF16>);
     return hipLaunchKernel(fn, dim3(static_cast<unsigned>(nwg)), dim3(kAttnThreads), args, 0, s);
 }
 

@@ -60,29 +60,6 @@ struct AttnArgs {
 };
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
-// The 16-bit element types the kernel takes: the MFMA operand vector, the
-// 32x32x16 MFMA with fp32 accumulation, and fp32 -> two packed elements
-// rounded to nearest even.
-struct AttnBF16 {
-    typedef bf16x8 frag;
-    __device__ static inline f32x16 mfma(frag a, frag b, f32x16 c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-    }
-    __device__ static inline uint32_t cvt2(float a, float b) { return IoBF16::cvt2(a, b); }
-};
-struct AttnF16 {
-    typedef f16x8 frag;
-    __device__ static inline f32x16 mfma(frag a, frag b, f32x16 c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-    }
-    __device__ static inline uint32_t cvt2(float a, float b) {
-        f32x2 f = {a, b};
-        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
-    }
-};
 
 // Two waves per SIMD (two workgroups per CU; LDS 70 KiB each): with one, a
 // wave's MFMA, exponential and LDS phases run back to back and the K/V loads
@@ -90,7 +67,7 @@ struct AttnF16 {
 // fits the kernel in 256 registers (no AGPRs, no spills) when asked to.
 template <class EL>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void attention_fwd_kernel(AttnArgs a) {
+void attention_fwd_kernel(AttnArgs a) {  // EL: MmaBF16 or MmaF16
     typedef typename EL::frag frag;
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kAttnBC * kKStride];
     __shared__ __attribute__((aligned(16))) uint16_t Vt[2][kAttnD * kVtStride];

@@ -76,6 +76,41 @@ struct IoBF16 {
     }
 };
 
+// 16-bit element types on the matrix cores (the Linear and attention
+// kernels): the MFMA operand vector (8 elements = 16 bytes), the 32x32x16
+// MFMA with fp32 accumulation, fp32 pairs -> two packed elements rounded to
+// nearest even, and single-element loads and stores.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+struct MmaBF16 {
+    typedef bf16x8 frag;
+    __device__ static inline f32x16 mfma(frag a, frag b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    __device__ static inline uint32_t cvt2(float a, float b) { return IoBF16::cvt2(a, b); }
+    __device__ static inline float load1(const void* p, int64_t i) { return IoBF16::load1(p, i); }
+    __device__ static inline void store1(void* p, int64_t i, float v) { IoBF16::store1(p, i, v); }
+};
+struct MmaF16 {
+    typedef f16x8 frag;
+    __device__ static inline f32x16 mfma(frag a, frag b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    __device__ static inline uint32_t cvt2(float a, float b) {
+        f32x2 f = {a, b};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+    }
+    __device__ static inline float load1(const void* p, int64_t i) {
+        return static_cast<float>(static_cast<const _Float16*>(p)[i]);
+    }
+    __device__ static inline void store1(void* p, int64_t i, float v) {
+        static_cast<uint16_t*>(p)[i] = static_cast<uint16_t>(cvt2(v, 0.0f) & 0xFFFFu);
+    }
+};
+
 // 16-byte global load/store; NT selects the non-temporal (streaming) hint.
 template <bool NT>
 __device__ inline u32x4 ld16(const u32x4* p) {

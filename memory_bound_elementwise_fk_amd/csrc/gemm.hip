@@ -33,17 +33,22 @@ int64_t linear_tiles(int64_t M, int64_t N) {
 
 hipError_t launch_linear_gelu(const void* x, const void* w, const void* bias, void* y, int64_t M,
                               int64_t N, int64_t K, int64_t ldx, int64_t ldw, int64_t ldy,
-                              int gelu, hipStream_t s) {
+                              int gelu, Dtype dt, hipStream_t s) {
     const int64_t tiles = linear_tiles(M, N);
     void* args[] = {const_cast<void**>(&x), const_cast<void**>(&w), const_cast<void**>(&bias), &y,
                     &M, &N, &K, &ldx, &ldw, &ldy, &gelu};
-    if (K % LinearDtlShape::BK == 0)
-        return hipLaunchKernel(reinterpret_cast<const void*>(&linear_gelu_dtl_kernel<LinearDtlShape>),
-                               dim3(static_cast<unsigned>(tiles)), dim3(LinearDtlShape::kThreads),
-                               args, 0, s);
-    return hipLaunchKernel(reinterpret_cast<const void*>(&linear_gelu_kernel<LinearShape>),
-                           dim3(static_cast<unsigned>(tiles)), dim3(LinearShape::kThreads), args, 0,
-                           s);
+    const bool f16 = dt == kF16;
+    if (K % LinearDtlShape::BK == 0) {
+        const void* fn =
+            f16 ? reinterpret_cast<const void*>(&linear_gelu_dtl_kernel<LinearDtlShape, MmaF16>)
+                : reinterpret_cast<const void*>(&linear_gelu_dtl_kernel<LinearDtlShape, MmaBF16>);
+        return hipLaunchKernel(fn, dim3(static_cast<unsigned>(tiles)),
+                               dim3(LinearDtlShape::kThreads), args, 0, s);
+    }
+    const void* fn = f16 ? reinterpret_cast<const void*>(&linear_gelu_kernel<LinearShape, MmaF16>)
+                         : reinterpret_cast<const void*>(&linear_gelu_kernel<LinearShape, MmaBF16>);
+    return hipLaunchKernel(fn, dim3(static_cast<unsigned>(tiles)), dim3(LinearShape::kThreads),
+                           args, 0, s);
 }
 
 }  // namespace fk

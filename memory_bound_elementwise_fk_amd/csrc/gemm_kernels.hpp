@@ -1,7 +1,7 @@
 // gemm_kernels.hpp -- Linear layer with a fused GELU epilogue on the gfx950
 // matrix cores: Y = GELU(X W^T + b), X [M, K], W [N, K] (a Linear weight:
-// one row per output feature), b [N], Y [M, N], bf16 in and out, fp32
-// accumulation.
+// one row per output feature), b [N], Y [M, N], bf16 or fp16 in and out,
+// fp32 accumulation.
 //
 // This is the Linear -> GELU part of the LayerNorm -> Linear -> GELU fusion
 // example of "Lecture 6: GPU Kernels and Triton", section 6.1: the product
@@ -35,8 +35,6 @@
 
 namespace fk {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int OCC_ = 1>
 struct GemmShape {
@@ -76,7 +74,7 @@ __device__ inline void gemm_tile_of(int64_t b, int64_t tiles_m, int64_t tiles_n,
     tn = r / rows;
 }
 
-template <class S>
+template <class S, class EL = MmaBF16>
 __global__ __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(S::kOcc, S::kOcc)))
 void linear_gelu_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
@@ -168,19 +166,18 @@ void linear_gelu_kernel(
         const uint16_t* b_base = &Bs[buf][(wn * S::WN + frag_row) * S::kStride + frag_k];
 #pragma unroll
         for (int kk = 0; kk < S::BK / 16; ++kk) {
-            bf16x8 af[S::kTM], bf[S::kTN];
+            typename EL::frag af[S::kTM], bf[S::kTN];
 #pragma unroll
             for (int i = 0; i < S::kTM; ++i)
-                af[i] = *reinterpret_cast<const bf16x8*>(a_base + i * 32 * S::kStride + kk * 16);
+                af[i] = *reinterpret_cast<const typename EL::frag*>(a_base + i * 32 * S::kStride + kk * 16);
 #pragma unroll
             for (int j = 0; j < S::kTN; ++j)
-                bf[j] = *reinterpret_cast<const bf16x8*>(b_base + j * 32 * S::kStride + kk * 16);
+                bf[j] = *reinterpret_cast<const typename EL::frag*>(b_base + j * 32 * S::kStride + kk * 16);
 #pragma unroll
             for (int i = 0; i < S::kTM; ++i)
 #pragma unroll
                 for (int j = 0; j < S::kTN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j],
-                                                                        0, 0, 0);
+                    acc[i][j] = EL::mfma(af[i], bf[j], acc[i][j]);
         }
         if (kt + 1 < nk) store_tiles(buf ^ 1);
         __syncthreads();
@@ -190,7 +187,7 @@ void linear_gelu_kernel(
 #pragma unroll
     for (int j = 0; j < S::kTN; ++j) {
         const int64_t col = n0 + wn * S::WN + j * 32 + lane % 32;
-        const float bv = (bias != nullptr && col < N) ? IoBF16::load1(bias, col) : 0.0f;
+        const float bv = (bias != nullptr && col < N) ? EL::load1(bias, col) : 0.0f;
 #pragma unroll
         for (int i = 0; i < S::kTM; ++i) {
             float v[16];
@@ -201,7 +198,7 @@ void linear_gelu_kernel(
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int64_t row = row0 + (e / 4) * 8 + e % 4;
-                if (row < M && col < N) IoBF16::store1(Y, row * ldy + col, v[e]);
+                if (row < M && col < N) EL::store1(Y, row * ldy + col, v[e]);
             }
         }
     }
@@ -266,7 +263,7 @@ __device__ constexpr int vmcnt_imm(int n) {
     return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8);
 }
 
-template <class S>
+template <class S, class EL = MmaBF16>
 __global__ __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(S::kOcc, S::kOcc)))
 void linear_gelu_dtl_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
                             const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y,
@@ -340,25 +337,24 @@ void linear_gelu_dtl_kernel(const uint16_t* __restrict__ X, const uint16_t* __re
 #pragma unroll
         for (int kk = 0; kk < S::BK / 16; ++kk) {
             const int c = kk * 2 + lane / 32;  // logical chunk of this lane's 8 k values
-            bf16x8 af[S::kTM], bf[S::kTN];
+            typename EL::frag af[S::kTM], bf[S::kTN];
 #pragma unroll
             for (int i = 0; i < S::kTM; ++i) {
                 const int r = wm * S::WM + i * 32 + frow;
-                af[i] = *reinterpret_cast<const bf16x8*>(stage + r * S::kRowBytes +
+                af[i] = *reinterpret_cast<const typename EL::frag*>(stage + r * S::kRowBytes +
                                                          ((c ^ ((r >> 2) & 3)) << 4));
             }
 #pragma unroll
             for (int j = 0; j < S::kTN; ++j) {
                 const int r = S::BM + wn * S::WN + j * 32 + frow;
-                bf[j] = *reinterpret_cast<const bf16x8*>(stage + r * S::kRowBytes +
+                bf[j] = *reinterpret_cast<const typename EL::frag*>(stage + r * S::kRowBytes +
                                                          ((c ^ ((r >> 2) & 3)) << 4));
             }
 #pragma unroll
             for (int i = 0; i < S::kTM; ++i)
 #pragma unroll
                 for (int j = 0; j < S::kTN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j],
-                                                                        0, 0, 0);
+                    acc[i][j] = EL::mfma(af[i], bf[j], acc[i][j]);
         }
     }
 
@@ -366,7 +362,7 @@ void linear_gelu_dtl_kernel(const uint16_t* __restrict__ X, const uint16_t* __re
 #pragma unroll
     for (int j = 0; j < S::kTN; ++j) {
         const int64_t col = n0 + wn * S::WN + j * 32 + lane % 32;
-        const float bv = (bias != nullptr && col < N) ? IoBF16::load1(bias, col) : 0.0f;
+        const float bv = (bias != nullptr && col < N) ? EL::load1(bias, col) : 0.0f;
 #pragma unroll
         for (int i = 0; i < S::kTM; ++i) {
             float v[16];
@@ -377,7 +373,7 @@ void linear_gelu_dtl_kernel(const uint16_t* __restrict__ X, const uint16_t* __re
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int64_t row = row0 + (e / 4) * 8 + e % 4;
-                if (row < M && col < N) IoBF16::store1(Y, row * ldy + col, v[e]);
+                if (row < M && col < N) EL::store1(Y, row * ldy + col, v[e]);
             }
         }
     }

@@ -286,11 +286,12 @@ def linear_gelu(x: np.ndarray, w: np.ndarray, bias: np.ndarray | None = None, ge
                 rows: np.ndarray | None = None) -> np.ndarray:
     """y = GELU(x w^T + bias) in double, rounded once to x's storage type.
 
-    x [M, K], w [N, K], bias [N] (float32, or bf16 as uint16 bits). The
-    product is numpy's float64 matmul of the stored values (a library
-    primitive used as one step); the bias is added in double, GELU is the
-    oracle's real tanh-GELU; the result is rounded to fp32 and, for bf16
-    data, then to bf16. ``rows`` selects a subset of rows of x (sampling).
+    x [M, K], w [N, K], bias [N] (float32, float16, or bf16 as uint16
+    bits). The product is numpy's float64 matmul of the stored values (a
+    library primitive used as one step); the bias is added in double, GELU
+    is the oracle's real tanh-GELU; the result is rounded to fp32 and, for
+    bf16 or fp16 data, then to that type (nearest even). ``rows`` selects a
+    subset of rows of x (sampling).
     """
     xd = _as_f64(x if rows is None else x[np.asarray(rows)])
     wd = _as_f64(w)
@@ -300,7 +301,9 @@ def linear_gelu(x: np.ndarray, w: np.ndarray, bias: np.ndarray | None = None, ge
     if gelu:
         acc = gelu_tanh_f64(acc).reshape(acc.shape)
     out = acc.astype(np.float32)
-    return f32_to_bf16(out).reshape(out.shape) if x.dtype == np.uint16 else out
+    if x.dtype == np.uint16:
+        return f32_to_bf16(out).reshape(out.shape)
+    return out.astype(np.float16) if x.dtype == np.float16 else out
 
 
 def linear_abs_bound(x: np.ndarray, w: np.ndarray, rows: np.ndarray | None = None) -> np.ndarray:

@@ -262,7 +262,7 @@ def test_attention_validation(L):
     assert f(A, B, C, D, 1, 1, 1 << 31, 128, good, 1, bf, None) == fk.FK_ERR_UNSUPPORTED
 
 
-def test_fp16_is_for_attention_only(L):
+def test_fp16_is_for_linear_and_attention_only(L):
     import ctypes
     f16 = fk.FK_F16
     C, D = 0x7F0000C00000, 0x7F0000E00000
@@ -279,8 +279,11 @@ def test_fp16_is_for_attention_only(L):
     assert L.fk_gelu_tanh_backward(A, B, C, 5, f16, None) == U
     assert L.fk_softmax_rows_backward(A, B, C, 4, 10, 10, 10, 10, f16, None) == U
     assert L.fk_softmax_backward_max_cols(f16) == U
-    assert L.fk_linear_gelu(A, B, None, C, 4, 10, 16, 16, 16, 10, 1, f16, None) == U
-    # attention takes it: the same validation as bf16
+    # Linear and attention take it: the same validation as bf16
+    li = L.fk_linear_gelu
+    assert li(A, B, None, C, 0, 10, 16, 16, 16, 10, 1, f16, None) == fk.FK_OK
+    assert li(A, B, None, C, 4, 10, 12, 16, 16, 10, 1, f16, None) == U          # K % 8
+    assert li(A, B, None, A + 32, 4, 10, 16, 16, 16, 10, 1, f16, None) == fk.FK_ERR_OVERLAP
     st = (ctypes.c_int64 * 12)(*([2 * 3 * 128, 3 * 128, 128] * 4))
     a = L.fk_attention_fwd
     assert a(A, B, C, D, 0, 3, 16, 128, st, 1, f16, None) == fk.FK_OK

@@ -7,7 +7,8 @@ order the matrix cores choose, so any summation order must pass:
 |y - r| <= ulp_bf16(|r|) + 1.13 (K + 2) 2^-24 ((|x| |w|^T)_ij + |b_j|)
 (the rounding of y to bf16, plus the worst-case fp32 accumulation error,
 through GELU's slope <= 1.13). As a sharper statistical check, at least
-99 % of the outputs must be within one bf16 ulp of the oracle.
+99 % of the outputs must be within one bf16 ulp of the oracle. fp16 data:
+the same with the fp16 ulp.
 """
 import numpy as np
 import pytest
@@ -26,28 +27,43 @@ def bf16_ulp(r):
     return np.exp2(e - 7)
 
 
-def operands(M, N, K, seed, bias=True):
+def fp16_ulp(r):
+    e = np.floor(np.log2(np.maximum(np.abs(r), 2.0 ** -14)))
+    return np.exp2(e - 10)
+
+
+def f64(a):
+    return oracle.bf16_to_f32(a).astype(np.float64) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
+def store(a, dt):
+    """float32 values -> the storage of dt (bf16 bits or float16)."""
+    a = np.asarray(a, np.float32)
+    return a.astype(np.float16) if dt == "fp16" else wl.f32_to_bf16_bits(a).reshape(a.shape)
+
+
+def operands(M, N, K, seed, bias=True, dt="bf16"):
     rng = np.random.default_rng(seed)
-    x = wl.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32)).reshape(M, K)
-    w = wl.f32_to_bf16_bits((rng.standard_normal((N, K)) / np.sqrt(max(K, 1)))
-                            .astype(np.float32)).reshape(N, K)
-    b = wl.f32_to_bf16_bits(rng.standard_normal(N).astype(np.float32)) if bias else None
+    x = store(rng.standard_normal((M, K)), dt)
+    w = store(rng.standard_normal((N, K)) / np.sqrt(max(K, 1)), dt)
+    b = store(rng.standard_normal(N), dt) if bias else None
     return x, w, b
 
 
 def check(got, x, w, b, gelu, what, rows=None):
     ref = oracle.linear_gelu(x, w, b, gelu=gelu, rows=rows)
-    g = oracle.bf16_to_f32(got).astype(np.float64)
-    r = oracle.bf16_to_f32(ref).astype(np.float64)
+    g = f64(got)
+    r = f64(ref)
+    ulp = fp16_ulp if x.dtype == np.float16 else bf16_ulp
     K = x.shape[1]
     scale = oracle.linear_abs_bound(x, w, rows=rows)
     if b is not None:
-        scale = scale + np.abs(oracle.bf16_to_f32(b).astype(np.float64))[None, :]
-    lim = bf16_ulp(r) + 1.13 * (K + 2) * 2.0 ** -24 * scale
+        scale = scale + np.abs(f64(b))[None, :]
+    lim = ulp(r) + 1.13 * (K + 2) * 2.0 ** -24 * scale
     err = np.abs(g - r)
     bad = np.flatnonzero(err > lim)
     assert bad.size == 0, f"{what}: {bad.size} beyond the bound, worst excess {(err - lim).max():.3e}"
-    within = np.mean(err <= bf16_ulp(r))
+    within = np.mean(err <= ulp(r))
     assert within >= 0.99, f"{what}: only {within:.4f} of outputs within one bf16 ulp"
 
 
@@ -58,10 +74,11 @@ def check(got, x, w, b, gelu, what, rows=None):
                                    (1, 1, 32), (33, 65, 96), (300, 200, 384), (257, 511, 1024),
                                    (513, 257, 4096)])
 @pytest.mark.parametrize("gelu", [True, False])
-def test_linear_shapes(M, N, K, gelu):
-    x, w, b = operands(M, N, K, seed=M * 7 + N + K)
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
+def test_linear_shapes(M, N, K, gelu, dt):
+    x, w, b = operands(M, N, K, seed=M * 7 + N + K, dt=dt)
     y = fk.linear_gelu(to_dev(x), to_dev(w), to_dev(b), gelu=gelu)
-    check(to_host(y), x, w, b, gelu, f"{M}x{N}x{K} gelu={gelu}")
+    check(to_host(y), x, w, b, gelu, f"{dt} {M}x{N}x{K} gelu={gelu}")
 
 
 def test_linear_without_bias_and_k_zero():
@@ -91,14 +108,15 @@ def test_linear_strided_operands(K):
     assert np.all(got[:, N:] == 0x7FC1), "row padding of y was written"
 
 
-def test_linear_mlp_shape_sampled_rows():
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
+def test_linear_mlp_shape_sampled_rows(dt):
     # the MLP up-projection shape the bench times: 8192 x 4096 -> 16384
     M, N, K = 8192, 16384, 4096
-    x, w, b = operands(M, N, K, seed=9)
+    x, w, b = operands(M, N, K, seed=9, dt=dt)
     y = fk.linear_gelu(to_dev(x), to_dev(w), to_dev(b))
     rows = np.sort(np.random.default_rng(10).choice(M, 48, replace=False))
     got = to_host(y[torch.from_numpy(rows).to(DEV)])
-    check(got, x, w, b, True, "8192x16384x4096 sampled rows", rows=rows)
+    check(got, x, w, b, True, f"{dt} 8192x16384x4096 sampled rows", rows=rows)
 
 
 def test_linear_is_bitwise_reproducible():

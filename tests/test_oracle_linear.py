@@ -5,7 +5,7 @@ step), so the pins target what could go wrong around it: the orientation
 (x w^T, w holding one row per output feature), the bias, the GELU and the
 rounding. Checked against a pure-Python triple loop on tiny shapes, torch's
 float64 linear + tanh-GELU, the identity and zero weights, and the rounding
-chain double -> fp32 -> bf16.
+chains double -> fp32 -> bf16 and double -> fp32 -> fp16.
 """
 import numpy as np
 import torch
@@ -67,3 +67,14 @@ def test_bf16_rounding_chain_and_row_sampling():
     assert np.array_equal(oracle.linear_gelu(x, w, b, rows=rows), full[rows])
     bound = oracle.linear_abs_bound(x, w, rows=rows)
     assert bound.shape == (3, 20) and np.all(bound >= np.abs(d[rows] - oracle.bf16_to_f32(b)))
+
+
+def test_fp16_rounding_chain():
+    x = RNG.standard_normal((10, 48)).astype(np.float16)
+    w = (RNG.standard_normal((14, 48)) * 0.1).astype(np.float16)
+    b = RNG.standard_normal(14).astype(np.float16)
+    got = oracle.linear_gelu(x, w, b)
+    assert got.dtype == np.float16 and got.shape == (10, 14)
+    ref = F.gelu(F.linear(*(torch.from_numpy(a.astype(np.float64)) for a in (x, w, b))),
+                 approximate="tanh").numpy()
+    assert np.array_equal(got, ref.astype(np.float32).astype(np.float16))
