@@ -56,7 +56,8 @@ typedef enum {
 typedef enum {
     FK_OP_ADD_SCALAR = 1, /* v = v + scalar               */
     FK_OP_MUL_SCALAR = 2, /* v = v * scalar               */
-    FK_OP_GELU_TANH = 3   /* v = tanh-GELU(v); scalar ignored */
+    FK_OP_GELU_TANH = 3,  /* v = tanh-GELU(v); scalar ignored */
+    FK_OP_RELU = 4        /* v = v > 0 ? v : +0, NaN kept; scalar ignored */
 } fk_op_kind;
 
 typedef struct {
@@ -219,13 +220,20 @@ int fk_softmax_rows_backward(const void* y, const void* dy, void* dx,
  * bf16), or FK_ERR_INVALID_ARG for an unknown dtype. Pure host query. */
 int64_t fk_softmax_backward_max_cols(int dtype);
 
+/* Epilogue activations of fk_linear_gelu. */
+typedef enum {
+    FK_ACT_NONE = 0,
+    FK_ACT_GELU_TANH = 1, /* the tanh-GELU of fk_gelu_tanh */
+    FK_ACT_RELU = 2       /* v > 0 ? v : +0, NaN kept     */
+} fk_activation;
+
 /*
- * Linear layer with a fused GELU epilogue on the matrix cores:
- * y[i][j] = GELU(sum_k x[i][k] w[j][k] + bias[j]) (or without GELU when
- * fuse_gelu is 0), i < M, j < N: the Linear -> GELU part of the LayerNorm ->
- * Linear -> GELU fusion example of "Lecture 6: GPU Kernels and Triton",
- * section 6.1, with the activation applied to the fp32 accumulators instead
- * of a second pass over the M x N product. x: M rows of K (row stride ldx),
+ * Linear layer with a fused activation epilogue on the matrix cores:
+ * y[i][j] = act(sum_k x[i][k] w[j][k] + bias[j]), i < M, j < N, act one of
+ * fk_activation (else FK_ERR_INVALID_ARG): the Linear -> GELU part of the
+ * LayerNorm -> Linear -> GELU fusion example of "Lecture 6: GPU Kernels and
+ * Triton", section 6.1, with the activation applied to the fp32
+ * accumulators instead of a second pass over the M x N product. x: M rows of K (row stride ldx),
  * w: N rows of K (a Linear weight, row stride ldw), bias: N values or NULL,
  * y: M rows of N (row stride ldy); all DEVICE memory of dtype. fp32
  * accumulation; y rounded once to the dtype (nearest even).
@@ -236,7 +244,7 @@ int64_t fk_softmax_backward_max_cols(int dtype);
  */
 int fk_linear_gelu(const void* x, const void* w, const void* bias, void* y,
                    int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldw,
-                   int64_t ldy, int fuse_gelu, int dtype, void* stream);
+                   int64_t ldy, int act, int dtype, void* stream);
 
 /*
  * FlashAttention forward: for every batch b < B and head h < H,

@@ -27,6 +27,11 @@ FK_ERR_HIP = -4
 FK_OP_ADD_SCALAR = 1
 FK_OP_MUL_SCALAR = 2
 FK_OP_GELU_TANH = 3
+FK_OP_RELU = 4
+FK_ACT_NONE = 0
+FK_ACT_GELU_TANH = 1
+FK_ACT_RELU = 2
+_ACTS = {"none": FK_ACT_NONE, "gelu_tanh": FK_ACT_GELU_TANH, "relu": FK_ACT_RELU}
 FK_MAX_OPS = 8
 
 __all__ = [
@@ -327,8 +332,12 @@ def fk_softmax_backward_max_cols(dtype) -> int:
     return int(v)
 
 
-def fk_linear_gelu(x, w, bias, y, gelu: bool = True, stream=None) -> None:
-    """y = GELU(x @ w.T + bias) for 2-D bf16 x [M, K], w [N, K], bias [N] or None, y [M, N]."""
+def fk_linear_gelu(x, w, bias, y, gelu: bool = True, stream=None, activation: str | None = None
+                   ) -> None:
+    """y = act(x @ w.T + bias) for 2-D bf16/fp16 x [M, K], w [N, K], bias [N] or None, y [M, N].
+
+    act is tanh-GELU (gelu=True) or none (gelu=False), or the named
+    ``activation`` ("none", "gelu_tanh", "relu") when given."""
     for t, name in ((x, "x"), (w, "w"), (y, "y")):
         _device_tensor(t, name)
         if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
@@ -345,10 +354,16 @@ def fk_linear_gelu(x, w, bias, y, gelu: bool = True, stream=None) -> None:
         if bias.dtype != x.dtype or bias.dim() != 1 or bias.numel() != N or not bias.is_contiguous():
             raise ValueError("fk_linear_gelu: bias must be a contiguous [N] tensor of x's dtype")
         b = bias.data_ptr()
+    if activation is None:
+        act = FK_ACT_GELU_TANH if gelu else FK_ACT_NONE
+    elif activation in _ACTS:
+        act = _ACTS[activation]
+    else:
+        raise ValueError(f"fk_linear_gelu: activation must be one of {sorted(_ACTS)}")
     ld = lambda t, n: t.stride(0) if t.shape[0] > 1 else n  # noqa: E731
     with _torch().cuda.device(x.device):
         _check(lib().fk_linear_gelu(x.data_ptr(), w.data_ptr(), b, y.data_ptr(), M, N, K,
-                                    ld(x, K), ld(w, K), ld(y, N), int(bool(gelu)),
+                                    ld(x, K), ld(w, K), ld(y, N), act,
                                     _dtype_code(x), _stream_handle(x, stream)), "fk_linear_gelu")
 
 
@@ -421,9 +436,9 @@ def softmax_rows_backward(y, dy, stream=None):
     return dx
 
 
-def linear_gelu(x, w, bias=None, gelu: bool = True, stream=None):
+def linear_gelu(x, w, bias=None, gelu: bool = True, stream=None, activation: str | None = None):
     y = _torch().empty((x.shape[0], w.shape[0]), dtype=x.dtype, device=x.device)
-    fk_linear_gelu(x, w, bias, y, gelu, stream)
+    fk_linear_gelu(x, w, bias, y, gelu, stream, activation)
     return y
 
 

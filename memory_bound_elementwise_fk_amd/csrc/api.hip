@@ -9,7 +9,7 @@
 
 static_assert(FK_MAX_OPS == fk::kMaxOps, "op list size mismatch");
 static_assert(int(FK_OP_ADD_SCALAR) == int(fk::kOpAdd) && int(FK_OP_MUL_SCALAR) == int(fk::kOpMul) &&
-                  int(FK_OP_GELU_TANH) == int(fk::kOpGelu),
+                  int(FK_OP_GELU_TANH) == int(fk::kOpGelu) && int(FK_OP_RELU) == int(fk::kOpRelu),
               "op kind mismatch");
 static_assert(int(FK_F32) == int(fk::kF32) && int(FK_BF16) == int(fk::kBF16) &&
                   int(FK_F16) == int(fk::kF16),
@@ -126,7 +126,8 @@ int fk_elementwise_chain(const void* x, void* y, int64_t n, int dtype, const fk_
     list.n = n_ops;
     for (int i = 0; i < n_ops; ++i) {
         const int32_t k = ops[i].kind;
-        if (k != FK_OP_ADD_SCALAR && k != FK_OP_MUL_SCALAR && k != FK_OP_GELU_TANH)
+        if (k != FK_OP_ADD_SCALAR && k != FK_OP_MUL_SCALAR && k != FK_OP_GELU_TANH &&
+            k != FK_OP_RELU)
             return FK_ERR_INVALID_ARG;
         list.kind[i] = k;
         list.scalar[i] = ops[i].scalar;
@@ -242,11 +243,12 @@ int64_t fk_softmax_backward_max_cols(int dtype) {
 }
 
 int fk_linear_gelu(const void* x, const void* w, const void* bias, void* y, int64_t M, int64_t N,
-                   int64_t K, int64_t ldx, int64_t ldw, int64_t ldy, int fuse_gelu, int dtype,
+                   int64_t K, int64_t ldx, int64_t ldw, int64_t ldy, int act, int dtype,
                    void* stream) {
     if (!dtype_ok(dtype) && !is_f16(dtype)) return FK_ERR_INVALID_ARG;
     if (M < 0 || N < 0 || K < 0) return FK_ERR_INVALID_ARG;
-    if (fuse_gelu != 0 && fuse_gelu != 1) return FK_ERR_INVALID_ARG;
+    if (act != FK_ACT_NONE && act != FK_ACT_GELU_TANH && act != FK_ACT_RELU)
+        return FK_ERR_INVALID_ARG;
     if (M == 0 || N == 0) return FK_OK;
     if (y == nullptr || (K > 0 && (x == nullptr || w == nullptr))) return FK_ERR_INVALID_ARG;
     if (ldy < N || (K > 0 && (ldx < K || ldw < K))) return FK_ERR_INVALID_ARG;
@@ -264,7 +266,7 @@ int fk_linear_gelu(const void* x, const void* w, const void* bias, void* y, int6
                   ranges_overlap(y, by, w, ((N - 1) * ldw + K) * 2)))
         return FK_ERR_OVERLAP;
     if (bias != nullptr && ranges_overlap(y, by, bias, N * 2)) return FK_ERR_OVERLAP;
-    return hip_status(fk::launch_linear_gelu(x, w, bias, y, M, N, K, ldx, ldw, ldy, fuse_gelu,
+    return hip_status(fk::launch_linear_gelu(x, w, bias, y, M, N, K, ldx, ldw, ldy, act,
                                              static_cast<fk::Dtype>(dtype),
                                              static_cast<hipStream_t>(stream)));
 }

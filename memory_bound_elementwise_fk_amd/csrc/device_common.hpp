@@ -191,6 +191,9 @@ __device__ inline void gelu_tanh_n(float (&v)[N]) {
     for (int j = 0; j < N; ++j) v[j] = y[j];
 }
 
+// ReLU: v for v > 0, else +0; NaN stays NaN (as torch's relu).
+__device__ inline float relu1(float v) { return (v > 0.0f || v != v) ? v : 0.0f; }
+
 // Derivative of the tanh-GELU (for the backward pass; derived from the
 // forward definition): with s = 1 / (1 + 2^t) (the logistic of 2u) and
 // q = 1 - s, GELU'(x) = s + w s q, w = 2 sqrt(2/pi) x (1 + 3 * 0.044715 x^2).

@@ -46,6 +46,9 @@ struct ChainOp {
             } else if (k == kOpMul) {
 #pragma unroll
                 for (int j = 0; j < N; ++j) v[j] = v[j] * s;
+            } else if (k == kOpRelu) {
+#pragma unroll
+                for (int j = 0; j < N; ++j) v[j] = relu1(v[j]);
             } else {
                 gelu_tanh_n(v);
             }

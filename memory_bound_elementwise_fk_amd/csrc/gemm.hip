@@ -33,10 +33,10 @@ int64_t linear_tiles(int64_t M, int64_t N) {
 
 hipError_t launch_linear_gelu(const void* x, const void* w, const void* bias, void* y, int64_t M,
                               int64_t N, int64_t K, int64_t ldx, int64_t ldw, int64_t ldy,
-                              int gelu, Dtype dt, hipStream_t s) {
+                              int act, Dtype dt, hipStream_t s) {
     const int64_t tiles = linear_tiles(M, N);
     void* args[] = {const_cast<void**>(&x), const_cast<void**>(&w), const_cast<void**>(&bias), &y,
-                    &M, &N, &K, &ldx, &ldw, &ldy, &gelu};
+                    &M, &N, &K, &ldx, &ldw, &ldy, &act};
     const bool f16 = dt == kF16;
     if (K % LinearDtlShape::BK == 0) {
         const void* fn =

@@ -35,6 +35,9 @@
 
 namespace fk {
 
+// epilogue activations of the Linear kernels (the codes of the C ABI)
+constexpr int kActNone = 0, kActGelu = 1, kActRelu = 2;
+
 
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int OCC_ = 1>
 struct GemmShape {
@@ -79,7 +82,7 @@ __global__ __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(S::
 void linear_gelu_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K,
-    int64_t ldx, int64_t ldw, int64_t ldy, int gelu) {
+    int64_t ldx, int64_t ldw, int64_t ldy, int act) {
     __shared__ __attribute__((aligned(16))) uint16_t As[2][S::BM * S::kStride];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][S::BN * S::kStride];
 
@@ -183,7 +186,7 @@ void linear_gelu_kernel(
         __syncthreads();
     }
 
-    // epilogue: + bias, GELU on the accumulators, round to bf16, store
+    // epilogue: + bias, the activation on the accumulators, round, store
 #pragma unroll
     for (int j = 0; j < S::kTN; ++j) {
         const int64_t col = n0 + wn * S::WN + j * 32 + lane % 32;
@@ -193,7 +196,12 @@ void linear_gelu_kernel(
             float v[16];
 #pragma unroll
             for (int e = 0; e < 16; ++e) v[e] = acc[i][j][e] + bv;
-            if (gelu) gelu_tanh_n(v);
+            if (act == kActGelu) {
+                gelu_tanh_n(v);
+            } else if (act == kActRelu) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) v[e] = relu1(v[e]);
+            }
             const int64_t row0 = m0 + wm * S::WM + i * 32 + (lane / 32) * 4;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
@@ -268,7 +276,7 @@ __global__ __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(S::
 void linear_gelu_dtl_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
                             const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y,
                             int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldw, int64_t ldy,
-                            int gelu) {
+                            int act) {
     __shared__ __attribute__((aligned(1024))) char smem[S::kStages * S::kStageBytes];
 
     const int64_t tiles_m = (M + S::BM - 1) / S::BM;
@@ -358,7 +366,7 @@ void linear_gelu_dtl_kernel(const uint16_t* __restrict__ X, const uint16_t* __re
         }
     }
 
-    // epilogue: + bias, GELU on the accumulators, round to bf16, store
+    // epilogue: + bias, the activation on the accumulators, round, store
 #pragma unroll
     for (int j = 0; j < S::kTN; ++j) {
         const int64_t col = n0 + wn * S::WN + j * 32 + lane % 32;
@@ -368,7 +376,12 @@ void linear_gelu_dtl_kernel(const uint16_t* __restrict__ X, const uint16_t* __re
             float v[16];
 #pragma unroll
             for (int e = 0; e < 16; ++e) v[e] = acc[i][j][e] + bv;
-            if (gelu) gelu_tanh_n(v);
+            if (act == kActGelu) {
+                gelu_tanh_n(v);
+            } else if (act == kActRelu) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) v[e] = relu1(v[e]);
+            }
             const int64_t row0 = m0 + wm * S::WM + i * 32 + (lane / 32) * 4;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {

@@ -10,7 +10,7 @@ namespace fk {
 
 constexpr int kMaxOps = 8;  // equals FK_MAX_OPS of the public header
 
-enum OpKind : int32_t { kOpAdd = 1, kOpMul = 2, kOpGelu = 3 };
+enum OpKind : int32_t { kOpAdd = 1, kOpMul = 2, kOpGelu = 3, kOpRelu = 4 };
 enum Dtype : int { kF32 = 0, kBF16 = 1, kF16 = 2 };  // kF16: Linear and attention only
 
 // Op list copied by value into the kernel arguments (no device copy).
@@ -58,12 +58,13 @@ hipError_t launch_softmax_backward(const void* y, const void* dy, void* dx, int6
                                    Dtype dt, hipStream_t s);
 int64_t softmax_backward_max_cols(Dtype dt);
 
-// Y = GELU(X W^T + b) (bf16 or fp16, fp32 accumulation on MFMA); arguments
+// Y = act(X W^T + b), act 0 none, 1 tanh-GELU, 2 ReLU (bf16 or fp16, fp32
+// accumulation on MFMA); arguments
 // validated by the caller: K, ldx, ldw multiples of 8, X and W 16-byte
 // aligned, linear_tiles(M, N) <= linear_max_tiles().
 hipError_t launch_linear_gelu(const void* x, const void* w, const void* bias, void* y, int64_t M,
                               int64_t N, int64_t K, int64_t ldx, int64_t ldw, int64_t ldy,
-                              int gelu, Dtype dt, hipStream_t s);
+                              int act, Dtype dt, hipStream_t s);
 int64_t linear_tiles(int64_t M, int64_t N);
 int64_t linear_max_tiles();
 

@@ -25,6 +25,7 @@ LIB_PATH = _HERE / "liboracle.so"
 OP_ADD_SCALAR = 1
 OP_MUL_SCALAR = 2
 OP_GELU_TANH = 3
+OP_RELU = 4
 
 _lib = None
 
@@ -283,8 +284,11 @@ def _as_f64(a: np.ndarray) -> np.ndarray:
 
 
 def linear_gelu(x: np.ndarray, w: np.ndarray, bias: np.ndarray | None = None, gelu: bool = True,
-                rows: np.ndarray | None = None) -> np.ndarray:
-    """y = GELU(x w^T + bias) in double, rounded once to x's storage type.
+                rows: np.ndarray | None = None, activation: str | None = None) -> np.ndarray:
+    """y = act(x w^T + bias) in double, rounded once to x's storage type.
+
+    act: tanh-GELU (gelu=True) or none, or the named ``activation`` ("none",
+    "gelu_tanh", "relu": x > 0 ? x : +0 with NaN kept).
 
     x [M, K], w [N, K], bias [N] (float32, float16, or bf16 as uint16
     bits). The product is numpy's float64 matmul of the stored values (a
@@ -298,8 +302,13 @@ def linear_gelu(x: np.ndarray, w: np.ndarray, bias: np.ndarray | None = None, ge
     acc = xd @ wd.T
     if bias is not None:
         acc = acc + _as_f64(bias)[None, :]
-    if gelu:
+    act = activation if activation is not None else ("gelu_tanh" if gelu else "none")
+    if act == "gelu_tanh":
         acc = gelu_tanh_f64(acc).reshape(acc.shape)
+    elif act == "relu":
+        acc = np.where((acc > 0) | np.isnan(acc), acc, 0.0)
+    elif act != "none":
+        raise ValueError(f"unknown activation {act!r}")
     out = acc.astype(np.float32)
     if x.dtype == np.uint16:
         return f32_to_bf16(out).reshape(out.shape)

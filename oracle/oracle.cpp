@@ -114,12 +114,16 @@ double gelu_grad_real(double x) {
 }
 
 // ---------------------------------------------------------------- chain ---
-enum OpKind { kAdd = 1, kMul = 2, kGelu = 3 };
+enum OpKind { kAdd = 1, kMul = 2, kGelu = 3, kRelu = 4 };
+
+// ReLU: x for x > 0, else +0; NaN stays NaN.
+double relu_real(double x) { return (x > 0.0 || std::isnan(x)) ? x : 0.0; }
 
 bool ops_valid(const int32_t* kinds, int n_ops) {
     if (n_ops < 1 || kinds == nullptr) return false;
     for (int i = 0; i < n_ops; ++i)
-        if (kinds[i] != kAdd && kinds[i] != kMul && kinds[i] != kGelu) return false;
+        if (kinds[i] != kAdd && kinds[i] != kMul && kinds[i] != kGelu && kinds[i] != kRelu)
+            return false;
     return true;
 }
 
@@ -132,6 +136,7 @@ float chain_one(float v, const int32_t* kinds, const float* scalars, int n_ops) 
             case kAdd: r = static_cast<double>(v) + static_cast<double>(scalars[i]); break;
             case kMul: r = static_cast<double>(v) * static_cast<double>(scalars[i]); break;
             case kGelu: r = gelu_real(static_cast<double>(v)); break;
+            case kRelu: r = relu_real(static_cast<double>(v)); break;
         }
         v = static_cast<float>(r);
     }

@@ -93,7 +93,8 @@ def test_chain_validation(L):
     assert c(A, B, 10, 0, None, 3, None) == fk.FK_ERR_INVALID_ARG
     assert c(A, B, 10, 0, good, 0, None) == fk.FK_ERR_INVALID_ARG
     assert c(A, B, 10, 0, _ops(*[(1, 0.0)] * 9), 9, None) == fk.FK_ERR_INVALID_ARG
-    assert c(A, B, 10, 0, _ops((4, 1.0)), 1, None) == fk.FK_ERR_INVALID_ARG
+    assert c(A, B, 10, 0, _ops((5, 1.0)), 1, None) == fk.FK_ERR_INVALID_ARG
+    assert c(A, B, 0, 0, _ops((fk.FK_OP_RELU, 0.0)), 1, None) == fk.FK_OK     # ReLU is a kind
     assert c(A, B, 10, 0, _ops((0, 1.0)), 1, None) == fk.FK_ERR_INVALID_ARG
     assert c(A, B, 10, 5, good, 3, None) == fk.FK_ERR_INVALID_ARG
     assert c(None, B, 10, 0, good, 3, None) == fk.FK_ERR_INVALID_ARG
@@ -219,7 +220,8 @@ def test_linear_validation(L):
     assert f(A, B, None, Y, 0, 10, 16, 16, 16, 10, 1, bf, None) == fk.FK_OK      # M == 0
     assert f(A, B, None, Y, 4, 0, 16, 16, 16, 10, 1, bf, None) == fk.FK_OK      # N == 0
     assert f(A, B, None, Y, -1, 10, 16, 16, 16, 10, 1, bf, None) == fk.FK_ERR_INVALID_ARG
-    assert f(A, B, None, Y, 4, 10, 16, 16, 16, 10, 2, bf, None) == fk.FK_ERR_INVALID_ARG
+    assert f(A, B, None, Y, 4, 10, 16, 16, 16, 10, 3, bf, None) == fk.FK_ERR_INVALID_ARG  # act
+    assert f(A, B, None, Y, 0, 10, 16, 16, 16, 10, fk.FK_ACT_RELU, bf, None) == fk.FK_OK
     assert f(A, B, None, Y, 4, 10, 16, 16, 16, 10, 1, 9, None) == fk.FK_ERR_INVALID_ARG
     assert f(A, B, None, None, 4, 10, 16, 16, 16, 10, 1, bf, None) == fk.FK_ERR_INVALID_ARG
     assert f(None, B, None, Y, 4, 10, 16, 16, 16, 10, 1, bf, None) == fk.FK_ERR_INVALID_ARG

@@ -156,6 +156,18 @@ def test_chain_add_mul_are_bit_exact(dt):
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_chain_relu_is_bit_exact(dt):
+    x = random_input((70_003,), dt, 3.0, seed=4)
+    if dt == "f32":
+        x[:6] = np.float32([0.0, -0.0, np.nan, np.inf, -np.inf, -1e-40])
+    ops = [(fk.FK_OP_ADD_SCALAR, -0.5), (fk.FK_OP_RELU, 0.0), (fk.FK_OP_MUL_SCALAR, 2.0)]
+    got = to_host(fk.elementwise_chain(to_dev(x), ops))
+    ref = oracle.chain(x, ops)
+    bits = np.uint16 if dt == "bf16" else np.uint32
+    assert np.array_equal(got.view(bits), ref.view(bits))
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("n", [1, 7, 4097, 50_001])
 def test_chain_long_op_lists(dt, n):
     x = random_input((n,), dt, 2.0, seed=n + 1)

@@ -81,6 +81,20 @@ def test_linear_shapes(M, N, K, gelu, dt):
     check(to_host(y), x, w, b, gelu, f"{dt} {M}x{N}x{K} gelu={gelu}")
 
 
+@pytest.mark.parametrize("M,N,K", [(300, 200, 392), (257, 511, 1024)])  # both main loops
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
+def test_linear_relu_epilogue(M, N, K, dt):
+    x, w, b = operands(M, N, K, seed=M + N + K + 1, dt=dt)
+    y = fk.linear_gelu(to_dev(x), to_dev(w), to_dev(b), activation="relu")
+    got = to_host(y)
+    ref = oracle.linear_gelu(x, w, b, activation="relu")
+    g, r = f64(got), f64(ref)
+    ulp = fp16_ulp if dt == "fp16" else bf16_ulp
+    scale = oracle.linear_abs_bound(x, w) + np.abs(f64(b))[None, :]
+    assert np.all(np.abs(g - r) <= ulp(r) + (K + 2) * 2.0 ** -24 * scale), f"relu {dt} {M}x{N}x{K}"
+    assert np.all(g >= 0) and not np.any(np.signbit(g)), "ReLU output must be +0 or positive"
+
+
 def test_linear_without_bias_and_k_zero():
     x, w, _ = operands(130, 70, 40, seed=3, bias=False)
     y = fk.linear_gelu(to_dev(x), to_dev(w), None)

@@ -8,6 +8,8 @@
   double GELU applied to numpy's fp32 x + 1, rounded by numpy.
 * fp32 -> bf16 nearest-even is pinned bit for bit against torch's own
   conversion over random bit patterns and hand-picked ties.
+* ReLU (an op of the chain and an epilogue of the Linear kernel) is exact:
+  x for x > 0, +0 otherwise, NaN kept, as torch's relu.
 """
 import json
 from pathlib import Path
@@ -119,3 +121,20 @@ def test_bf16_widening_is_exact():
     allbits = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
     w = oracle.bf16_to_f32(allbits)
     assert np.array_equal(w.view(np.uint32), allbits.astype(np.uint32) << 16)
+
+
+def test_relu_is_exact_and_keeps_nan():
+    rng = np.random.default_rng(14)
+    x = np.concatenate([rng.standard_normal(100_000).astype(np.float32),
+                        np.float32([0.0, -0.0, 1e-40, -1e-40, np.inf, -np.inf, np.nan])])
+    got = oracle.chain(x, [(oracle.OP_RELU, 0.0)])
+    ref = torch.relu(torch.from_numpy(x)).numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(x))
+    ok = ~np.isnan(x)
+    assert np.array_equal(got[ok], ref[ok])
+    assert np.all(np.signbit(got[ok]) == False)   # -0 and negatives give +0  # noqa: E712
+    # a chain with ReLU inside: 2 * relu(x - 1), each op an fp32 kernel
+    two = oracle.chain(x[ok], [(oracle.OP_ADD_SCALAR, -1.0), (oracle.OP_RELU, 0.0),
+                               (oracle.OP_MUL_SCALAR, 2.0)])
+    want = np.maximum(x[ok] + np.float32(-1.0), np.float32(0.0)) * np.float32(2.0)
+    assert np.array_equal(two, want)

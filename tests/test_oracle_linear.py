@@ -78,3 +78,14 @@ def test_fp16_rounding_chain():
     ref = F.gelu(F.linear(*(torch.from_numpy(a.astype(np.float64)) for a in (x, w, b))),
                  approximate="tanh").numpy()
     assert np.array_equal(got, ref.astype(np.float32).astype(np.float16))
+
+
+def test_relu_epilogue_matches_torch():
+    x = RNG.standard_normal((11, 24))
+    w = RNG.standard_normal((7, 24))
+    b = RNG.standard_normal(7)
+    got = oracle.linear_gelu(x, w, b, activation="relu")
+    ref = torch.relu(F.linear(torch.from_numpy(x), torch.from_numpy(w), torch.from_numpy(b)))
+    assert np.array_equal(got, ref.numpy().astype(np.float32))
+    assert np.array_equal(oracle.linear_gelu(x, w, b, activation="none"),
+                          oracle.linear_gelu(x, w, b, gelu=False))
