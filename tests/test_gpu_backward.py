@@ -128,6 +128,27 @@ def test_gelu_backward_bf16_large():
     gelu_bwd_check(x, dy, "bf16", "bf16 2^26")
 
 
+def test_gelu_backward_bf16_beyond_one_launch_grid():
+    # 2^34 + 1001 bf16 elements (32 GiB per tensor, x, dy and dx: 96 GiB):
+    # more tiles than one launch's 2^31 work-items, so the kernel strides
+    # over tiles; checked on sampled outputs (random, first tiles, ragged tail)
+    n = (1 << 34) + 1001
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(7)
+    x = torch.randn(n, dtype=torch.bfloat16, device=DEV, generator=gen).mul_(3)
+    dy = torch.randn(n, dtype=torch.bfloat16, device=DEV, generator=gen)
+    dx = torch.empty_like(x)
+    fk.fk_gelu_tanh_backward(x, dy, dx)
+    rng = np.random.default_rng(8)
+    idx = np.unique(np.concatenate([rng.integers(0, n, 1 << 20), np.arange(5000),
+                                    np.arange(n - 5000, n)]))
+    it = torch.from_numpy(idx).to(DEV)
+    xs, dys, dxs = (wl.from_torch(t[it]) for t in (x, dy, dx))
+    del x, dy, dx
+    torch.cuda.empty_cache()
+    gelu_bwd_check(xs, dys, "bf16", "bf16 2^34 + 1001, sampled", dx=dxs)
+
+
 # ---------------------------------------------------------- softmax bwd ---
 def softmax_pair(rows, cols, dt, seed, scale=3.0):
     x = random_input((rows, cols), dt, scale, seed=seed)

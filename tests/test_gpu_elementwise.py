@@ -127,6 +127,29 @@ def test_c5b_gelu_bf16_full_size():
     assert_bf16(got, oracle.gelu_tanh(x, threads=T), "C5b")
 
 
+def _sample_indices(n, seed):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([rng.integers(0, n, 1 << 20), np.arange(5000),
+                                     np.arange(n - 5000, n)]))
+
+
+def test_gelu_bf16_beyond_one_launch_grid():
+    # 2^34 + 1001 bf16 elements (32 GiB per tensor): more tiles than one
+    # launch's 2^31 work-items, so the kernel strides over tiles; checked on
+    # sampled outputs (random, the first tiles, the ragged tail)
+    n = (1 << 34) + 1001
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(5)
+    x = torch.randn(n, dtype=torch.bfloat16, device=DEV, generator=gen).mul_(3)
+    y = torch.empty_like(x)
+    fk.fk_gelu_tanh(x, y)
+    it = torch.from_numpy(_sample_indices(n, 6)).to(DEV)
+    xs, ys = wl.from_torch(x[it]), wl.from_torch(y[it])
+    del x, y
+    torch.cuda.empty_cache()
+    assert_bf16(ys, oracle.gelu_tanh(xs), "GELU bf16 2^34 + 1001, sampled")
+
+
 # ----------------------------------------------------------------- chain --
 def test_c3_chain_fused_full_size_and_unfused_equal():
     x = wl.make_input("C3")
