@@ -233,3 +233,20 @@ def test_softmax_backward_identities():
     assert np.all(run_sbwd(onehot, dy, "f32") == 0)                    # exactly zero
     const = run_sbwd(y, np.full((rows, cols), 0.75, np.float32), "f32")
     assert np.abs(const).max() <= 2e-6
+
+
+def test_softmax_backward_rows_beyond_one_launch_grid():
+    # 2^25 + 5 rows of 3 fp32 columns: the kernel strides over rows
+    rows, cols = (1 << 25) + 5, 3
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(21)
+    y = torch.softmax(torch.randn(rows, cols, device=DEV, generator=gen) * 2, dim=1)
+    dy = torch.randn(rows, cols, device=DEV, generator=gen)
+    dx = fk.softmax_rows_backward(y, dy)
+    rng = np.random.default_rng(22)
+    idx = np.unique(np.concatenate([rng.integers(0, rows, 200_000), np.arange(rows - 100, rows)]))
+    it = torch.from_numpy(idx).to(DEV)
+    ys, dys, dxs = (wl.from_torch(t[it]) for t in (y, dy, dx))
+    del y, dy, dx
+    torch.cuda.empty_cache()
+    sbwd_check(dxs, ys, dys, "f32", f"softmax backward {rows}x{cols}, sampled rows")

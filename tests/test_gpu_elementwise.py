@@ -150,6 +150,21 @@ def test_gelu_bf16_beyond_one_launch_grid():
     assert_bf16(ys, oracle.gelu_tanh(xs), "GELU bf16 2^34 + 1001, sampled")
 
 
+def test_chain_fp32_beyond_one_launch_grid():
+    # 2^33 + 3 fp32 elements (32 GiB per tensor): the fp32 tiles stride too
+    n = (1 << 33) + 3
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(9)
+    x = torch.rand(n, dtype=torch.float32, device=DEV, generator=gen).mul_(12).sub_(6)
+    y = torch.empty_like(x)
+    fk.fk_elementwise_chain(x, y, C3)
+    it = torch.from_numpy(_sample_indices(n, 10)).to(DEV)
+    xs, ys = wl.from_torch(x[it]), wl.from_torch(y[it])
+    del x, y
+    torch.cuda.empty_cache()
+    assert_gelu_f32(ys, oracle.chain(xs, C3), "chain fp32 2^33 + 3, sampled")
+
+
 # ----------------------------------------------------------------- chain --
 def test_c3_chain_fused_full_size_and_unfused_equal():
     x = wl.make_input("C3")

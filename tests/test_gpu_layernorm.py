@@ -196,3 +196,22 @@ def test_layernorm_bitwise_reproducible():
     a = fk.layernorm_rows(x, gelu=True)
     c = fk.layernorm_rows(x, gelu=True)
     assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+
+
+@pytest.mark.parametrize("cols", [1, 3])
+def test_layernorm_rows_beyond_one_launch_grid(cols):
+    # 2^25 + 5 rows of 1 or 3 fp32 columns: the kernel strides over rows
+    rows = (1 << 25) + 5
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(cols + 10)
+    x = torch.randn(rows, cols, dtype=torch.float32, device=DEV, generator=gen).mul_(3)
+    g, b = params(cols, "f32", cols)
+    y = fk.layernorm_rows(x, to_dev(g), to_dev(b), gelu=True)
+    rng = np.random.default_rng(cols + 10)
+    idx = np.unique(np.concatenate([rng.integers(0, rows, 200_000), np.arange(rows - 100, rows)]))
+    it = torch.from_numpy(idx).to(DEV)
+    xs, ys = wl.from_torch(x[it]), wl.from_torch(y[it])
+    del x, y
+    torch.cuda.empty_cache()
+    assert_ln(ys, oracle.layernorm_rows(xs, g, b, gelu=True), "f32", cols, g, b, True,
+              f"layernorm {rows}x{cols}, sampled rows")

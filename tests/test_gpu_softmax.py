@@ -202,3 +202,21 @@ def test_softmax_runs_are_bitwise_reproducible():
         PATHS[path](x, y1)
         PATHS[path](x, y2)
         assert torch.equal(y1.view(torch.int32), y2.view(torch.int32)), path
+
+
+@pytest.mark.parametrize("cols", [1, 3])
+def test_softmax_rows_beyond_one_launch_grid(cols):
+    # 2^25 + 5 rows of 1 or 3 fp32 columns: more workgroups than one launch's
+    # 2^31 work-items hold, so the kernel strides over rows; sampled rows
+    rows = (1 << 25) + 5
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(cols)
+    x = torch.randn(rows, cols, dtype=torch.float32, device=DEV, generator=gen).mul_(3)
+    y = fk.softmax_rows(x)
+    rng = np.random.default_rng(cols)
+    idx = np.unique(np.concatenate([rng.integers(0, rows, 200_000), np.arange(rows - 100, rows)]))
+    it = torch.from_numpy(idx).to(DEV)
+    xs, ys = wl.from_torch(x[it]), wl.from_torch(y[it])
+    del x, y
+    torch.cuda.empty_cache()
+    check("f32", ys, oracle.softmax_rows(xs), f"softmax {rows}x{cols}, sampled rows")
