@@ -1,6 +1,8 @@
 // backward.hip -- launchers of the backward kernels (backward_kernels.hpp):
 // GELU backward (elementwise, two inputs) and row softmax backward.
 #include "backward_kernels.hpp"
+#include <utility>
+
 #include "launch.hpp"
 
 namespace fk {
@@ -49,7 +51,8 @@ hipError_t launch_ew2(const void* a, const void* b, void* out, int64_t n, const 
 struct BwdShape {
     int wpr, vpl;
 };
-constexpr BwdShape kBwdShapes[] = {{1, 1}, {1, 2}, {1, 4}, {2, 4}, {4, 4}, {8, 4}, {16, 4}};
+constexpr BwdShape kBwdShapes[] = {{1, 1}, {1, 2}, {1, 4}, {3, 2}, {2, 4},  {5, 2}, {3, 4},
+                                   {4, 4}, {5, 4}, {6, 4}, {8, 4}, {12, 4}, {16, 4}};
 constexpr int kNumBwdShapes = sizeof(kBwdShapes) / sizeof(kBwdShapes[0]);
 
 template <class IO>
@@ -64,13 +67,29 @@ hipError_t launch_sbwd(const void* y, const void* dy, void* dx, int64_t rows, in
     constexpr int kRowsPerWg = kThreads / (WPR * kWave);
     int64_t grid = (rows + kRowsPerWg - 1) / kRowsPerWg;
     if (grid > kMaxWorkItems / kThreads) grid = kMaxWorkItems / kThreads;
-    // a row that fills the shape exactly runs the variant without masks
-    const bool full = vec && cols == bwd_capacity<IO>(BwdShape{WPR, VPL});
+    // a row that fills the shape exactly runs the variant without masks; a
+    // width that is a multiple of the vector, the one with per-vector masks
     const void* fn =
-        full ? reinterpret_cast<const void*>(&softmax_bwd_reg_kernel<IO, WPR, VPL, true, true, true>)
-        : vec ? reinterpret_cast<const void*>(&softmax_bwd_reg_kernel<IO, WPR, VPL, true, true>)
-              : reinterpret_cast<const void*>(&softmax_bwd_reg_kernel<IO, WPR, VPL, false>);
+        !vec ? reinterpret_cast<const void*>(&softmax_bwd_reg_kernel<IO, WPR, VPL, false>)
+        : cols == bwd_capacity<IO>(BwdShape{WPR, VPL})
+            ? reinterpret_cast<const void*>(&softmax_bwd_reg_kernel<IO, WPR, VPL, true, true, kFitFull>)
+        : cols % IO::kVec == 0
+            ? reinterpret_cast<const void*>(&softmax_bwd_reg_kernel<IO, WPR, VPL, true, true, kFitVec>)
+            : reinterpret_cast<const void*>(&softmax_bwd_reg_kernel<IO, WPR, VPL, true, true>);
     return launch_kernel(fn, grid, kThreads, s, y, dy, dx, rows, cols, ldy, lddy, lddx);
+}
+
+template <class IO, size_t... I>
+hipError_t dispatch_sbwd(int shape, const void* y, const void* dy, void* dx, int64_t rows,
+                         int64_t cols, int64_t ldy, int64_t lddy, int64_t lddx, bool vec,
+                         hipStream_t s, std::index_sequence<I...>) {
+    hipError_t r = hipErrorInvalidValue;
+    ((shape == static_cast<int>(I)
+          ? (r = launch_sbwd<IO, kBwdShapes[I].wpr, kBwdShapes[I].vpl>(y, dy, dx, rows, cols, ldy,
+                                                                      lddy, lddx, vec, s))
+          : r),
+     ...);
+    return r;
 }
 
 template <class IO>
@@ -82,15 +101,8 @@ hipError_t launch_sbwd_t(const void* y, const void* dy, void* dx, int64_t rows, 
                      (lddy * IO::kBytes) % 16 == 0 && (lddx * IO::kBytes) % 16 == 0;
     int shape = 0;
     while (shape < kNumBwdShapes - 1 && cols > bwd_capacity<IO>(kBwdShapes[shape])) ++shape;
-    switch (shape) {
-        case 0: return launch_sbwd<IO, 1, 1>(y, dy, dx, rows, cols, ldy, lddy, lddx, vec, s);
-        case 1: return launch_sbwd<IO, 1, 2>(y, dy, dx, rows, cols, ldy, lddy, lddx, vec, s);
-        case 2: return launch_sbwd<IO, 1, 4>(y, dy, dx, rows, cols, ldy, lddy, lddx, vec, s);
-        case 3: return launch_sbwd<IO, 2, 4>(y, dy, dx, rows, cols, ldy, lddy, lddx, vec, s);
-        case 4: return launch_sbwd<IO, 4, 4>(y, dy, dx, rows, cols, ldy, lddy, lddx, vec, s);
-        case 5: return launch_sbwd<IO, 8, 4>(y, dy, dx, rows, cols, ldy, lddy, lddx, vec, s);
-        default: return launch_sbwd<IO, 16, 4>(y, dy, dx, rows, cols, ldy, lddy, lddx, vec, s);
-    }
+    return dispatch_sbwd<IO>(shape, y, dy, dx, rows, cols, ldy, lddy, lddx, vec, s,
+                             std::make_index_sequence<kNumBwdShapes>{});
 }
 
 }  // namespace

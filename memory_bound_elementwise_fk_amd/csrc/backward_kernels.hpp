@@ -86,16 +86,17 @@ __global__ __launch_bounds__(T) void ew2_scalar_kernel(const void* a, const void
 // as softmax_reg_kernel): dot = sum y dy, dx = y (dy - dot). dx may be y or
 // dy exactly (with the same stride): every value is in registers before the
 // row is written.
-// FULL: the launcher guarantees cols == WPR * 64 * VPL * V (no masking code).
-template <class IO, int WPR, int VPL, bool VEC, bool NT = false, bool FULL = false>
+// FIT: what the launcher guarantees about the width (kFitFull: no masking
+// code; kFitVec: masks per vector; kFitAny: per value).
+template <class IO, int WPR, int VPL, bool VEC, bool NT = false, int FIT = kFitAny>
 __global__ __launch_bounds__(reg_threads<WPR>()) void softmax_bwd_reg_kernel(
     const void* y, const void* dy, void* dx, int64_t rows, int64_t cols, int64_t ldy,
     int64_t lddy, int64_t lddx) {
     constexpr int E = VPL * IO::kVec;
     constexpr int kRowLanes = WPR * kWave;
     constexpr int kRowsPerWg = reg_threads<WPR>() / kRowLanes;
-    static_assert(!FULL || VEC, "full rows are a vector-layout case");
-    const int64_t span_cols = FULL ? int64_t(kRowLanes) * E : cols;
+    static_assert(FIT == kFitAny || VEC, "fitted rows are a vector-layout case");
+    const int64_t span_cols = FIT == kFitFull ? int64_t(kRowLanes) * E : cols;
     // per-wave partial dot products, alternating halves row by row: one
     // barrier per row (a half is rewritten two rows later, after every wave
     // has passed the barrier of the row in between)
@@ -113,9 +114,14 @@ __global__ __launch_bounds__(reg_threads<WPR>()) void softmax_bwd_reg_kernel(
         const bool active = row < rows;
         float vy[E], vg[E];
         if (active) {
-            load_span2<IO, VPL, kRowLanes, VEC, NT>(row_ptr<IO>(y, row, ldy),
-                                                    row_ptr<IO>(dy, row, lddy), span_cols, 0, lr,
-                                                    vy, vg, 0.0f);
+            if constexpr (FIT == kFitVec)
+                load_span2_vfit<IO, VPL, kRowLanes, NT>(row_ptr<IO>(y, row, ldy),
+                                                        row_ptr<IO>(dy, row, lddy), cols, lr, vy,
+                                                        vg);
+            else
+                load_span2<IO, VPL, kRowLanes, VEC, NT>(row_ptr<IO>(y, row, ldy),
+                                                        row_ptr<IO>(dy, row, lddy), span_cols, 0,
+                                                        lr, vy, vg, 0.0f);
         } else {
 #pragma unroll
             for (int i = 0; i < E; ++i) vy[i] = vg[i] = 0.0f;
@@ -133,9 +139,13 @@ __global__ __launch_bounds__(reg_threads<WPR>()) void softmax_bwd_reg_kernel(
         }
 #pragma unroll
         for (int i = 0; i < E; ++i) vg[i] = vy[i] * (vg[i] - d);
-        if (active)
-            store_span<IO, VPL, kRowLanes, VEC, NT>(row_ptr<IO>(dx, row, lddx), span_cols, 0, lr,
-                                                    vg);
+        if (active) {
+            if constexpr (FIT == kFitVec)
+                store_span_vfit<IO, VPL, kRowLanes, NT>(row_ptr<IO>(dx, row, lddx), cols, lr, vg);
+            else
+                store_span<IO, VPL, kRowLanes, VEC, NT>(row_ptr<IO>(dx, row, lddx), span_cols, 0,
+                                                        lr, vg);
+        }
     }
 }
 

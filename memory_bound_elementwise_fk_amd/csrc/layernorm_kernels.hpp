@@ -58,11 +58,26 @@ __device__ inline void affine_chunk(const char* gp, const char* bp, int64_t cols
 // epilogue, which keeps the register count of the widest rows bounded.
 constexpr int kLnHoldAffineVpl = 2;
 
-// FULL: the launcher guarantees cols == WPR * 64 * VPL * V (the row fills
-// the shape exactly, on the vector layout), so no masking code is compiled;
-// ragged rows take FULL = false.
-template <class IO, int WPR, int VPL, bool VEC, bool GELU, bool NT = false, bool FULL = false>
-__global__ __launch_bounds__(reg_threads<WPR>()) void layernorm_reg_kernel(
+// Waves per SIMD the registers are budgeted for: two workgroups per CU where
+// a workgroup of more than 8 waves would otherwise run alone (12 waves leave
+// each SIMD 3), provided that costs at most 80 VGPRs (6 waves), gamma and
+// beta are held (VPL <= 2) and the row is full (the masks of other widths
+// would spill: measured 1.4-2x slower); 1 (no constraint) otherwise.
+template <int WPR, int VPL, int FIT>
+constexpr int ln_min_waves() {
+    constexpr int per_simd = (reg_threads<WPR>() / kWave + 3) / 4;
+    return (FIT == kFitFull && VPL <= kLnHoldAffineVpl && per_simd > 2 && 2 * per_simd <= 6)
+               ? 2 * per_simd
+               : 1;
+}
+
+// FIT (kFitAny, kFitVec, kFitFull) is what the launcher guarantees about the
+// width: kFitFull (cols == WPR * 64 * VPL * V on the vector layout) compiles
+// no masks; kFitVec (cols a multiple of V on the vector layout) masks whole
+// vectors with tests that do not depend on the row; kFitAny masks values.
+template <class IO, int WPR, int VPL, bool VEC, bool GELU, bool NT = false, int FIT = kFitAny>
+__global__ __launch_bounds__(reg_threads<WPR>())
+__attribute__((amdgpu_waves_per_eu(ln_min_waves<WPR, VPL, FIT>()))) void layernorm_reg_kernel(
     const void* x, void* y, int64_t rows, int64_t cols, int64_t ldx, int64_t ldy,
     const void* gamma, const void* beta, float eps) {
     constexpr int V = IO::kVec;
@@ -81,11 +96,17 @@ __global__ __launch_bounds__(reg_threads<WPR>()) void layernorm_reg_kernel(
     const int wave = lr / kWave;
     const int lane = threadIdx.x % kWave;
     const int slot = sub * WPR;
-    static_assert(!FULL || VEC, "full rows are a vector-layout case");
+    static_assert(FIT == kFitAny || VEC, "fitted rows are a vector-layout case");
+    constexpr bool kFull = FIT == kFitFull;
+    constexpr bool kVfit = FIT == kFitVec;
     // the column count as the masked helpers see it: a compile-time constant
     // for full rows, so their masked paths fold away
-    const int64_t span_cols = FULL ? int64_t(kRowLanes) * E : cols;
+    const int64_t span_cols = kFull ? int64_t(kRowLanes) * E : cols;
     const bool full = span_cols >= int64_t(kRowLanes) * E;  // every value of every lane is a column
+    // kFitVec: which of this lane's vectors are columns (the same for every row)
+    bool in_row[VPL];
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) in_row[k] = (int64_t(k) * kRowLanes + lr) * V < cols;
     const float n = static_cast<float>(cols);
     const char* gp = static_cast<const char*>(gamma);
     const char* bp = static_cast<const char*>(beta);
@@ -94,7 +115,18 @@ __global__ __launch_bounds__(reg_threads<WPR>()) void layernorm_reg_kernel(
     // end are computed but never stored, so their values do not matter)
     float g[kHold ? E : 1], b[kHold ? E : 1];
     if constexpr (kHold) {
-        if (gp && bp) {
+        if constexpr (kVfit) {
+            if (gp) load_span_vfit<IO, VPL, kRowLanes>(gp, cols, lr, g, 1.0f);
+            if (bp) load_span_vfit<IO, VPL, kRowLanes>(bp, cols, lr, b, 0.0f);
+            if (!gp) {
+#pragma unroll
+                for (int i = 0; i < E; ++i) g[i] = 1.0f;
+            }
+            if (!bp) {
+#pragma unroll
+                for (int i = 0; i < E; ++i) b[i] = 0.0f;
+            }
+        } else if (gp && bp) {
             load_span2<IO, VPL, kRowLanes, VEC>(gp, bp, span_cols, 0, lr, g, b, 0.0f);
         } else {
 #pragma unroll
@@ -114,8 +146,11 @@ __global__ __launch_bounds__(reg_threads<WPR>()) void layernorm_reg_kernel(
         const bool active = row < rows;
         float v[E];
         if (active) {
-            load_span<IO, VPL, kRowLanes, VEC, NT>(row_ptr<IO>(x, row, ldx), span_cols, 0, lr, v,
-                                                  0.0f);
+            if constexpr (kVfit)
+                load_span_vfit<IO, VPL, kRowLanes, NT>(row_ptr<IO>(x, row, ldx), cols, lr, v, 0.0f);
+            else
+                load_span<IO, VPL, kRowLanes, VEC, NT>(row_ptr<IO>(x, row, ldx), span_cols, 0, lr,
+                                                      v, 0.0f);
         } else {
 #pragma unroll
             for (int i = 0; i < E; ++i) v[i] = 0.0f;
@@ -138,7 +173,15 @@ __global__ __launch_bounds__(reg_threads<WPR>()) void layernorm_reg_kernel(
         // deviations, their sum (the correction) and their squares; columns
         // past the row end (only in a ragged row) contribute 0
         float a = 0.0f, q = 0.0f;
-        if (full) {
+        if (kVfit) {
+#pragma unroll
+            for (int i = 0; i < E; ++i) {
+                const float d = in_row[i / V] ? v[i] - mu : 0.0f;
+                v[i] = d;
+                a += d;
+                q = fmaf(d, d, q);
+            }
+        } else if (full) {
 #pragma unroll
             for (int i = 0; i < E; ++i) {
                 const float d = v[i] - mu;
@@ -201,8 +244,13 @@ __global__ __launch_bounds__(reg_threads<WPR>()) void layernorm_reg_kernel(
 #pragma unroll
             for (int e = 0; e < V; ++e) v[k * V + e] = t[e];
         }
-        if (active)
-            store_span<IO, VPL, kRowLanes, VEC, NT>(row_ptr<IO>(y, row, ldy), span_cols, 0, lr, v);
+        if (active) {
+            if constexpr (kVfit)
+                store_span_vfit<IO, VPL, kRowLanes, NT>(row_ptr<IO>(y, row, ldy), cols, lr, v);
+            else
+                store_span<IO, VPL, kRowLanes, VEC, NT>(row_ptr<IO>(y, row, ldy), span_cols, 0, lr,
+                                                       v);
+        }
     }
 }
 

@@ -3,6 +3,8 @@
 // two-pass kernel above it.
 #include <atomic>
 
+#include <utility>
+
 #include "launch.hpp"
 #include "softmax_kernels.hpp"
 
@@ -26,15 +28,18 @@ int64_t clamp_grid(int64_t g, int threads) {
 }
 
 // Single-pass shapes (waves per row, 16-byte vectors per lane), smallest
-// first; the first that covers the row is used. At most 4 vectors per lane
-// until the widest shape: on MI355X a bf16 4096-column row ran 12 % faster
-// as 2 waves x 4 vectors than as 1 wave x 8 (fewer VGPRs, more waves in
-// flight).
+// capacity first; the first that covers the row is used. At most 4 vectors
+// per lane until the widest shape: on MI355X a bf16 4096-column row ran 12 %
+// faster as 2 waves x 4 vectors than as 1 wave x 8 (fewer VGPRs, more waves
+// in flight). The 3-, 5-, 6- and 12-wave shapes fit common model widths
+// exactly (bf16 3072, 5120, 6144, 10240, 12288, 24576; fp32 1536, 2560,
+// 3072, 5120, 6144, 12288): lanes left idle by a wider shape cost bandwidth
+// in proportion, a row's time being set by latency.
 struct RegShape {
     int wpr, vpl;
 };
-constexpr RegShape kRegShapes[] = {{1, 1}, {1, 2}, {1, 4}, {2, 4},
-                                   {4, 4}, {8, 4}, {16, 4}, {16, 8}};
+constexpr RegShape kRegShapes[] = {{1, 1}, {1, 2}, {1, 4},  {3, 2},  {2, 4},  {5, 2},  {3, 4},
+                                   {4, 4}, {5, 4}, {6, 4},  {8, 4},  {12, 4}, {16, 4}, {16, 8}};
 // Row data is read once and written once: non-temporal loads and stores
 // (measured 4-9 % faster on the C4 and C5a shapes).
 constexpr bool kRowNT = true;
@@ -51,28 +56,36 @@ hipError_t launch_reg(const void* x, void* y, int64_t rows, int64_t cols, int64_
     constexpr int kThreads = reg_threads<WPR>();
     constexpr int kRowsPerWg = kThreads / (WPR * kWave);
     const int64_t grid = clamp_grid((rows + kRowsPerWg - 1) / kRowsPerWg, kThreads);
-    // a row that fills the shape exactly runs the variant without masks
-    const bool full = vec && cols == reg_capacity<IO>(RegShape{WPR, VPL});
+    // a row that fills the shape exactly runs the variant without masks; a
+    // width that is a multiple of the vector, the one with per-vector masks
     const void* fn =
-        full ? reinterpret_cast<const void*>(&softmax_reg_kernel<IO, WPR, VPL, true, kRowNT, true>)
-        : vec ? reinterpret_cast<const void*>(&softmax_reg_kernel<IO, WPR, VPL, true, kRowNT>)
-              : reinterpret_cast<const void*>(&softmax_reg_kernel<IO, WPR, VPL, false>);
+        !vec ? reinterpret_cast<const void*>(&softmax_reg_kernel<IO, WPR, VPL, false>)
+        : cols == reg_capacity<IO>(RegShape{WPR, VPL})
+            ? reinterpret_cast<const void*>(&softmax_reg_kernel<IO, WPR, VPL, true, kRowNT, kFitFull>)
+        : cols % IO::kVec == 0
+            ? reinterpret_cast<const void*>(&softmax_reg_kernel<IO, WPR, VPL, true, kRowNT, kFitVec>)
+            : reinterpret_cast<const void*>(&softmax_reg_kernel<IO, WPR, VPL, true, kRowNT>);
     return launch_kernel(fn, grid, kThreads, s, x, y, rows, cols, ldx, ldy);
+}
+
+template <class IO, size_t... I>
+hipError_t dispatch_reg_i(int shape, const void* x, void* y, int64_t rows, int64_t cols,
+                          int64_t ldx, int64_t ldy, bool vec, hipStream_t s,
+                          std::index_sequence<I...>) {
+    hipError_t r = hipErrorInvalidValue;
+    ((shape == static_cast<int>(I)
+          ? (r = launch_reg<IO, kRegShapes[I].wpr, kRegShapes[I].vpl>(x, y, rows, cols, ldx, ldy,
+                                                                     vec, s))
+          : r),
+     ...);
+    return r;
 }
 
 template <class IO>
 hipError_t dispatch_reg(int shape, const void* x, void* y, int64_t rows, int64_t cols,
                         int64_t ldx, int64_t ldy, bool vec, hipStream_t s) {
-    switch (shape) {
-        case 0: return launch_reg<IO, 1, 1>(x, y, rows, cols, ldx, ldy, vec, s);
-        case 1: return launch_reg<IO, 1, 2>(x, y, rows, cols, ldx, ldy, vec, s);
-        case 2: return launch_reg<IO, 1, 4>(x, y, rows, cols, ldx, ldy, vec, s);
-        case 3: return launch_reg<IO, 2, 4>(x, y, rows, cols, ldx, ldy, vec, s);
-        case 4: return launch_reg<IO, 4, 4>(x, y, rows, cols, ldx, ldy, vec, s);
-        case 5: return launch_reg<IO, 8, 4>(x, y, rows, cols, ldx, ldy, vec, s);
-        case 6: return launch_reg<IO, 16, 4>(x, y, rows, cols, ldx, ldy, vec, s);
-        default: return launch_reg<IO, 16, 8>(x, y, rows, cols, ldx, ldy, vec, s);
-    }
+    return dispatch_reg_i<IO>(shape, x, y, rows, cols, ldx, ldy, vec, s,
+                              std::make_index_sequence<kNumRegShapes>{});
 }
 
 // Online shape: 1024 lanes per row, 16 values per lane per chunk.

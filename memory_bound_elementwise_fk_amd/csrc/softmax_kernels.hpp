@@ -159,27 +159,98 @@ __device__ inline void store_span(char* yr, int64_t cols, int64_t c0, int lane,
     }
 }
 
-// Workgroup size of the single-pass kernel: at least 256 lanes, several
-// rows per workgroup when a row takes fewer lanes.
+// A row whose width is a multiple of V, on the vector layout: each of a
+// lane's vectors lies wholly inside or wholly outside the row, so a mask is
+// one test per vector, the same for every row. All loads of the span are
+// issued before any is unpacked (as on the unmasked path); vectors past the
+// row end read as `fill`.
+template <class IO, int VPL, int LANES, bool NT = false>
+__device__ inline void load_span_vfit(const char* xr, int64_t cols, int lane,
+                                      float (&v)[VPL * IO::kVec], float fill) {
+    constexpr int V = IO::kVec;
+    u32x4 w[VPL];
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+        const int64_t c = (int64_t(k) * LANES + lane) * V;
+        w[k] = c < cols ? ld16<NT>(reinterpret_cast<const u32x4*>(xr + c * IO::kBytes))
+                        : u32x4{0u, 0u, 0u, 0u};
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+        IO::unpack(w[k], &v[k * V]);
+        if ((int64_t(k) * LANES + lane) * V >= cols) {
+#pragma unroll
+            for (int e = 0; e < V; ++e) v[k * V + e] = fill;
+        }
+    }
+}
+
+// Two rows' spans (e.g. y and dy) on the same columns, all loads of both in
+// flight before any is unpacked; vectors past the row end read as 0.
+template <class IO, int VPL, int LANES, bool NT = false>
+__device__ inline void load_span2_vfit(const char* ar, const char* br, int64_t cols, int lane,
+                                       float (&va)[VPL * IO::kVec], float (&vb)[VPL * IO::kVec]) {
+    constexpr int V = IO::kVec;
+    u32x4 wa[VPL], wb[VPL];
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+        const int64_t c = (int64_t(k) * LANES + lane) * V;
+        const bool in = c < cols;
+        wa[k] = in ? ld16<NT>(reinterpret_cast<const u32x4*>(ar + c * IO::kBytes))
+                   : u32x4{0u, 0u, 0u, 0u};
+        wb[k] = in ? ld16<NT>(reinterpret_cast<const u32x4*>(br + c * IO::kBytes))
+                   : u32x4{0u, 0u, 0u, 0u};
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+        IO::unpack(wa[k], &va[k * V]);
+        IO::unpack(wb[k], &vb[k * V]);
+    }
+}
+
+template <class IO, int VPL, int LANES, bool NT = false>
+__device__ inline void store_span_vfit(char* yr, int64_t cols, int lane,
+                                       const float (&v)[VPL * IO::kVec]) {
+    constexpr int V = IO::kVec;
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+        const int64_t c = (int64_t(k) * LANES + lane) * V;
+        if (c < cols) st16<NT>(reinterpret_cast<u32x4*>(yr + c * IO::kBytes), IO::pack(&v[k * V]));
+    }
+}
+
+// How a row fits its shape (a template argument of the row kernels):
+// kFitAny  any width, any alignment (masks per value where needed);
+// kFitVec  width a multiple of the vector on the vector layout (masks per
+//          vector, row-independent);
+// kFitFull width equal to the shape's capacity on the vector layout (no
+//          masks compiled).
+constexpr int kFitAny = 0, kFitVec = 1, kFitFull = 2;
+
+// Workgroup size of the single-pass kernels: whole rows, 256 lanes when a
+// row takes fewer (several rows per workgroup), else one row.
 template <int WPR>
 constexpr int reg_threads() {
-    return WPR * kWave > 256 ? WPR * kWave : 256;
+    return (WPR * kWave >= 256 ? 1 : 256 / (WPR * kWave)) * WPR * kWave;
 }
 
 // ------------------------------------------------- single-pass kernel -----
-// FULL: the launcher guarantees cols == WPR * 64 * VPL * V (the row fills the
-// shape exactly, on the vector layout), so no masking code is compiled (the
-// masks of ragged rows otherwise hold enough SGPRs to cost a wave per SIMD).
-template <class IO, int WPR, int VPL, bool VEC, bool NT = false, bool FULL = false>
+// FIT: what the launcher guarantees about the width (kFitAny, kFitVec,
+// kFitFull). Full rows compile no masking code (the masks of ragged rows
+// otherwise hold enough SGPRs to cost a wave per SIMD); kFitVec rows mask
+// whole vectors (they read as -inf, whose numerators are 0).
+template <class IO, int WPR, int VPL, bool VEC, bool NT = false, int FIT = kFitAny>
 __global__ __launch_bounds__(reg_threads<WPR>()) void softmax_reg_kernel(
     const void* x, void* y, int64_t rows, int64_t cols, int64_t ldx, int64_t ldy) {
     constexpr int V = IO::kVec;
     constexpr int E = VPL * V;
     constexpr int kRowLanes = WPR * kWave;
     constexpr int kRowsPerWg = reg_threads<WPR>() / kRowLanes;
-    static_assert(!FULL || VEC, "full rows are a vector-layout case");
+    static_assert(FIT == kFitAny || VEC, "fitted rows are a vector-layout case");
     // the column count as the masked helpers see it (a constant for full rows)
-    const int64_t span_cols = FULL ? int64_t(kRowLanes) * E : cols;
+    const int64_t span_cols = FIT == kFitFull ? int64_t(kRowLanes) * E : cols;
     // per-wave partials of the row max ([0]) and sum ([1]); one barrier per
     // reduction: a slot is rewritten only on the next row, after every wave
     // has passed the other reduction's barrier, i.e. finished reading it
@@ -198,7 +269,12 @@ __global__ __launch_bounds__(reg_threads<WPR>()) void softmax_reg_kernel(
         const bool active = row < rows;
         float v[E];
         if (active) {
-            load_span<IO, VPL, kRowLanes, VEC, NT>(row_ptr<IO>(x, row, ldx), span_cols, 0, lr, v);
+            if constexpr (FIT == kFitVec)
+                load_span_vfit<IO, VPL, kRowLanes, NT>(row_ptr<IO>(x, row, ldx), cols, lr, v,
+                                                       kNegInf);
+            else
+                load_span<IO, VPL, kRowLanes, VEC, NT>(row_ptr<IO>(x, row, ldx), span_cols, 0, lr,
+                                                      v);
         } else {
 #pragma unroll
             for (int i = 0; i < E; ++i) v[i] = kNegInf;
@@ -237,8 +313,13 @@ __global__ __launch_bounds__(reg_threads<WPR>()) void softmax_reg_kernel(
         const float r = 1.0f / s;
 #pragma unroll
         for (int i = 0; i < E; ++i) v[i] *= r;
-        if (active)
-            store_span<IO, VPL, kRowLanes, VEC, NT>(row_ptr<IO>(y, row, ldy), span_cols, 0, lr, v);
+        if (active) {
+            if constexpr (FIT == kFitVec)
+                store_span_vfit<IO, VPL, kRowLanes, NT>(row_ptr<IO>(y, row, ldy), cols, lr, v);
+            else
+                store_span<IO, VPL, kRowLanes, VEC, NT>(row_ptr<IO>(y, row, ldy), span_cols, 0, lr,
+                                                       v);
+        }
     }
 }
 

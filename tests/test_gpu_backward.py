@@ -172,10 +172,11 @@ def run_sbwd(y, dy, dt):
     return got
 
 
-# ragged widths, and every width that fills a row shape exactly (the
-# unmasked kernel variant) for both dtypes
-SCOLS = [1, 2, 3, 63, 64, 65, 256, 512, 1000, 1023, 1024, 1025, 2048, 4096, 4097, 8192, 16384,
-         16385, 32768]
+# ragged widths; widths that fill a row shape exactly (the unmasked kernel
+# variant, also of the 3-, 5-, 6- and 12-wave shapes) for both dtypes;
+# multiples of the vector inside a shape (the per-vector masks)
+SCOLS = [1, 2, 3, 63, 64, 65, 256, 512, 1000, 1023, 1024, 1025, 1536, 2048, 2560, 3000, 3072,
+         4096, 4097, 5000, 5120, 6144, 8192, 10240, 12000, 12288, 16384, 16385, 24576, 32768]
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])

@@ -89,10 +89,13 @@ def run(x, dt, g=None, b=None, gelu=False, eps=1e-5):
     return got
 
 
-# ragged widths, and every width that fills a row shape exactly (256 * 2^k:
-# the unmasked kernel variant) for both dtypes
-COLS = [1, 2, 3, 63, 64, 65, 255, 256, 512, 1000, 1023, 1024, 1025, 2048, 4095, 4096, 4097, 8192,
-        8193, 16384, 32768, 65536]
+# ragged widths; widths that fill a row shape exactly (256 * 2^k, and 768 ...
+# 24576 for the 3-, 5-, 6-, 10- and 12-wave shapes: the unmasked kernel
+# variant) for both dtypes; multiples of the vector inside a shape (1000,
+# 3000, 5000, 12000: the per-vector masks)
+COLS = [1, 2, 3, 63, 64, 65, 255, 256, 512, 768, 1000, 1023, 1024, 1025, 1280, 1536, 2048, 2560,
+        3000, 3072, 4095, 4096, 4097, 5000, 5120, 6144, 8192, 8193, 10240, 12000, 12288, 16384,
+        24576, 32768, 65536]
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])

@@ -67,10 +67,13 @@ def test_c5a_softmax_fp32_full_size_self_managed():
 
 
 # ------------------------------------------------------------- shapes -----
-# ragged widths, and every width that fills a single-pass row shape exactly
-# (256 * 2^k: the unmasked kernel variant) for both dtypes
-COLS = [1, 2, 3, 5, 63, 64, 65, 255, 256, 257, 512, 1000, 1023, 1024, 1025, 2047, 2048, 2049,
-        4095, 4096, 4097, 8192, 8193, 16384, 16385, 32768, 32769, 65536, 65537, 100_003]
+# ragged widths; widths that fill a single-pass row shape exactly (256 * 2^k,
+# and 1536 ... 24576 for the 3-, 5-, 6- and 12-wave shapes: the unmasked
+# kernel variant) for both dtypes; multiples of the vector inside a shape
+# (1000, 3000, 5000, 12000: the per-vector masks)
+COLS = [1, 2, 3, 5, 63, 64, 65, 255, 256, 257, 512, 1000, 1023, 1024, 1025, 1536, 2047, 2048, 2049,
+        2560, 3000, 3072, 4095, 4096, 4097, 5000, 5120, 6144, 8192, 8193, 10240, 12000, 12288,
+        16384, 16385, 24576, 32768, 32769, 65536, 65537, 100_003]
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
