@@ -12,8 +12,9 @@
 //
 // MI355X mapping. Each wave owns 32 queries; a workgroup of W waves owns
 // 32 W queries of one (batch, head) and walks the key blocks of 64 keys,
-// staged through LDS (K as [key][dim], V transposed as [dim][key], both
-// double-buffered, loaded one block ahead through registers). The wave
+// staged through LDS (K and V both as [key][dim], double-buffered, copied
+// one block ahead by direct global-to-LDS loads: no registers, no ALU). The
+// wave
 // computes the transposed scores S^T = K Q^T with the 32x32x16 bf16 MFMA:
 // K is the A operand (lane l: key l % 32, dims (l / 32) * 8 + e), Q the B
 // operand (query l % 32), held in registers for the whole key loop. In the
@@ -25,9 +26,14 @@
 // straight from the lane's S^T registers (rounded to bf16) -- the MFMA's
 // k index g * 8 + e (g = l / 32) is taken to mean key 8 (e / 4) + 4 g + e % 4
 // of each 16-key chunk, which is the order the accumulator layout holds
-// them in, and V^T's A fragments are read from LDS in the same key order
-// (two 8-byte runs). The output accumulator O^T again holds one query per
-// lane, so the final division by l is per lane.
+// them in. V^T's A fragments (lane l: dim l % 32, those 8 keys) come from
+// the row-major V block through the transposing LDS read of gfx950
+// (ds_read_b64_tr_b16): in each group of 16 lanes, lane 4a + b receives
+// element b of the 8-byte runs that lanes a, a + 4, a + 8, a + 12 address
+// (checked on the device), so lanes pointing at 4 consecutive keys of one
+// 4-dim run hand every lane 4 consecutive keys of its dim -- two such reads
+// per fragment. The output accumulator O^T again holds one query per lane,
+// so the final division by l is per lane.
 #pragma once
 
 #include "device_common.hpp"
@@ -40,10 +46,24 @@ constexpr int kAttnBC = 64;       // keys per block
 constexpr int kAttnWaves = 4;     // waves per workgroup (32 queries each)
 constexpr int kAttnThreads = kAttnWaves * kWave;
 constexpr int kAttnBQ = kAttnWaves * 32;
-constexpr int kKStride = kAttnD + 8;    // bf16 per K row in LDS (16 bytes of padding)
-constexpr int kVtStride = kAttnBC + 8;  // bf16 per V^T row in LDS
-constexpr int kAttnChunks = kAttnBC * kAttnD / 8;               // 16-byte chunks per block
-constexpr int kAttnLoads = kAttnChunks / kAttnThreads;          // per thread, per operand
+constexpr int kAttnRowBytes = kAttnD * 2;                       // one key row of K or V
+constexpr int kAttnBlockBytes = kAttnBC * kAttnRowBytes;        // 16 KiB per operand
+// direct loads per wave, per operand and block (each fills 1 KiB = 4 rows)
+constexpr int kAttnDmaPerWave = kAttnBlockBytes / 1024 / kAttnWaves;
+static_assert(kAttnDmaPerWave * 1024 * kAttnWaves == kAttnBlockBytes, "whole wave loads");
+// LDS layout of a block: row r (key) holds its 16 chunks of 16 bytes (8
+// dims each) permuted, chunk c at position c ^ swz(r): K with r % 16 (the
+// S^T fragment reads, 16 consecutive keys of one chunk per 256 bytes, hit
+// all 64 banks), V with 4 (r % 4) (the transposing reads, 4 consecutive
+// keys x 4 chunks per 256 bytes, hit all 64 banks).
+__device__ inline int attn_swz_k(int r) { return r & 15; }
+__device__ inline int attn_swz_v(int r) { return (r & 3) * 4; }
+// The running max m moves only when a block's max exceeds it by more than
+// this (log2 units): the numerators 2^(s - m) then stay below 2^8, and the
+// output acc / l does not depend on which m was subtracted, so it is the
+// same softmax. Random scores raise the max in most blocks by a little; each
+// raise costs a rescale of the 64 accumulator values of the lane.
+constexpr float kAttnMaxSlack = 8.0f;
 
 struct AttnArgs {
     const uint16_t* q;
@@ -60,6 +80,14 @@ struct AttnArgs {
 };
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// transposing 8-byte LDS read (see the lane rule above)
+__device__ inline u32x2 lds_read_tr16(const uint16_t* p) {
+    const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(p));
+    return __builtin_bit_cast(u32x2, r);
+}
 
 // Two waves per SIMD (two workgroups per CU; LDS 70 KiB each): with one, a
 // wave's MFMA, exponential and LDS phases run back to back and the K/V loads
@@ -69,8 +97,8 @@ template <class EL>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attention_fwd_kernel(AttnArgs a) {  // EL: MmaBF16 or MmaF16
     typedef typename EL::frag frag;
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kAttnBC * kKStride];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[2][kAttnD * kVtStride];
+    __shared__ __attribute__((aligned(1024))) uint16_t Ks[2][kAttnBC * kAttnD];
+    __shared__ __attribute__((aligned(1024))) uint16_t Vs[2][kAttnBC * kAttnD];
 
     // One workgroup per (query block, head), numbered level by level with the
     // heads fastest: level 0 holds every head's longest causal block. The
@@ -112,59 +140,42 @@ void attention_fwd_kernel(AttnArgs a) {  // EL: MmaBF16 or MmaF16
     const int64_t kend = a.causal ? q_last : a.T;
     const int64_t nkb = (kend + kAttnBC - 1) / kAttnBC;
 
-    // Staging. K: thread tid moves chunks c = tid + i * threads (key c / 16,
-    // dims (c % 16) * 8 .. + 8), stored row-major. V is stored transposed
-    // (V^T[dim][key]); thread tid takes the key pair 2 p, 2 p + 1
-    // (p = tid % 32) and dims 8 (tid / 32 + 8 i) .. + 8, and writes each dim
-    // of the pair as one 32-bit word: the 64 lanes of a wave then write 32
-    // consecutive words of one V^T row and 32 of the row 8 dims further
-    // (1152 bytes apart, the other half of the banks), without conflicts.
-    constexpr int kVPairs = kAttnBC / 2;                            // 32 key pairs
-    constexpr int kVRounds = (kAttnD / 8) / (kAttnThreads / kVPairs);  // dim blocks per thread
-    u32x4 rk[kAttnLoads], rv[2 * kVRounds];
-    auto load_block = [&](int64_t kb0) {
+    // Staging: wave w's direct load j of a block fills rows 4 (4 w + j) ..
+    // + 3 of K (and of V); lane i writes position i % 16 of row i / 16 of
+    // those, so it fetches the logical chunk at that position. The lane's
+    // source offsets within a block are fixed (kept per load); a block wholly
+    // inside T adds its first row, the last partial one clamps rows past T to
+    // row T - 1 (valid memory; those keys are masked, p = 0). LDS addresses
+    // are wave-uniform (scalar).
+    const int drow = lane / 16, dpos = lane % 16;
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    const uint32_t ks_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((las_ptr)(&Ks[0][0])));
+    const uint32_t vs_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((las_ptr)(&Vs[0][0])));
+    int64_t koff[kAttnDmaPerWave], voff[kAttnDmaPerWave];  // element offsets within a block
 #pragma unroll
-        for (int i = 0; i < kAttnLoads; ++i) {
-            const int c = tid + i * kAttnThreads;
-            const int64_t key = kb0 + c / (kAttnD / 8);
-            const int dim = (c % (kAttnD / 8)) * 8;
-            rk[i] = key < a.T ? *reinterpret_cast<const u32x4*>(Kg + key * a.kt + dim)
-                              : u32x4{0u, 0u, 0u, 0u};
-        }
+    for (int j = 0; j < kAttnDmaPerWave; ++j) {
+        const int r = (wave * kAttnDmaPerWave + j) * 4 + drow;
+        koff[j] = r * a.kt + (dpos ^ attn_swz_k(r)) * 8;
+        voff[j] = r * a.vt + (dpos ^ attn_swz_v(r)) * 8;
+    }
+    auto issue_block = [&](int64_t kb0, int buf) {
+        const bool whole = kb0 + kAttnBC <= a.T;
+        const uint16_t* kblk = Kg + kb0 * a.kt;
+        const uint16_t* vblk = Vg + kb0 * a.vt;
 #pragma unroll
-        for (int i = 0; i < kVRounds; ++i) {
-            const int64_t key = kb0 + 2 * (tid % kVPairs);
-            const int dim = 8 * (tid / kVPairs + i * (kAttnThreads / kVPairs));
-            rv[2 * i] = key < a.T ? *reinterpret_cast<const u32x4*>(Vg + key * a.vt + dim)
-                                  : u32x4{0u, 0u, 0u, 0u};
-            rv[2 * i + 1] = key + 1 < a.T
-                                ? *reinterpret_cast<const u32x4*>(Vg + (key + 1) * a.vt + dim)
-                                : u32x4{0u, 0u, 0u, 0u};
-        }
-    };
-    auto store_block = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < kAttnLoads; ++i) {
-            const int c = tid + i * kAttnThreads;
-            const int key = c / (kAttnD / 8);
-            const int dim = (c % (kAttnD / 8)) * 8;
-            *reinterpret_cast<u32x4*>(&Ks[buf][key * kKStride + dim]) = rk[i];
-        }
-#pragma unroll
-        for (int i = 0; i < kVRounds; ++i) {
-            const int key = 2 * (tid % kVPairs);
-            const int dim = 8 * (tid / kVPairs + i * (kAttnThreads / kVPairs));
-            const uint32_t a0[4] = {rv[2 * i].x, rv[2 * i].y, rv[2 * i].z, rv[2 * i].w};
-            const uint32_t a1[4] = {rv[2 * i + 1].x, rv[2 * i + 1].y, rv[2 * i + 1].z,
-                                    rv[2 * i + 1].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                // dims dim + 2e (low halves) and dim + 2e + 1 (high halves)
-                *reinterpret_cast<uint32_t*>(&Vt[buf][(dim + 2 * e) * kVtStride + key]) =
-                    (a0[e] & 0xFFFFu) | (a1[e] << 16);
-                *reinterpret_cast<uint32_t*>(&Vt[buf][(dim + 2 * e + 1) * kVtStride + key]) =
-                    (a0[e] >> 16) | (a1[e] & 0xFFFF0000u);
+        for (int j = 0; j < kAttnDmaPerWave; ++j) {
+            const uint32_t off = static_cast<uint32_t>(
+                buf * kAttnBlockBytes + (wave_s * kAttnDmaPerWave + j) * 1024);
+            const uint16_t* ksrc = kblk + koff[j];
+            const uint16_t* vsrc = vblk + voff[j];
+            if (!whole) {
+                const int r = (wave * kAttnDmaPerWave + j) * 4 + drow;
+                const int64_t key = kb0 + r < a.T ? kb0 + r : a.T - 1;
+                ksrc = Kg + key * a.kt + (dpos ^ attn_swz_k(r)) * 8;
+                vsrc = Vg + key * a.vt + (dpos ^ attn_swz_v(r)) * 8;
             }
+            lds_dma16(ksrc, ks_base + off);
+            lds_dma16(vsrc, vs_base + off);
         }
     };
 
@@ -174,13 +185,21 @@ void attention_fwd_kernel(AttnArgs a) {  // EL: MmaBF16 or MmaF16
     float m = -__builtin_inff();
     float l = 0.0f;
 
-    load_block(0);
-    store_block(0);
+    // fragment addressing of this lane: S^T reads key row (t * 32 + lane % 32)
+    // at chunk 2 kk + g; the V^T reads (two per fragment) take row k0 + e of
+    // 4-dim run 4 a of the lane's 16-dim half, e = (lane % 16) / 4,
+    // a = lane % 4, half = (lane / 16) % 2
+    const int vt_e = (lane % 16) / 4, vt_a = lane % 4, vt_half = (lane / 16) % 2;
+
+    issue_block(0, 0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
     for (int64_t kb = 0; kb < nkb; ++kb) {
         const int buf = static_cast<int>(kb & 1);
         const int64_t kb0 = kb * kAttnBC;
-        if (kb + 1 < nkb) load_block(kb0 + kAttnBC);
+        // the other buffer was last read in the previous block, which every
+        // wave has left (the barrier at its end)
+        if (kb + 1 < nkb) issue_block(kb0 + kAttnBC, buf ^ 1);
 
         // a causal block wholly above this wave's queries contributes nothing
         // (its last key block can be): the wave skips it (uniform branch)
@@ -189,14 +208,16 @@ void attention_fwd_kernel(AttnArgs a) {  // EL: MmaBF16 or MmaF16
             // that consecutive MFMAs are independent (a lone tile is a chain
             // of 8 dependent MFMAs, each also waiting on its LDS read)
             f32x16 s[2] = {f32x16{}, f32x16{}};
-            const uint16_t* kbase = &Ks[buf][(lane % 32) * kKStride + g * 8];
+            const int kr = lane % 32;  // + t * 32: the same swizzle (r % 16)
+            const uint16_t* kbase = &Ks[buf][kr * kAttnD];
 #pragma unroll
             for (int kk = 0; kk < kAttnD / 16; ++kk)
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
-                    s[t] = EL::mfma(
-                        *reinterpret_cast<const frag*>(kbase + t * 32 * kKStride + kk * 16),
-                        qf[kk], s[t]);
+                    s[t] = EL::mfma(*reinterpret_cast<const frag*>(
+                                        kbase + t * 32 * kAttnD +
+                                        (((2 * kk + g) ^ attn_swz_k(kr)) * 8)),
+                                    qf[kk], s[t]);
 
             // mask (only blocks that reach past T or, causal, past the wave's
             // first query), then the block max over the query's 32 keys, in
@@ -217,7 +238,9 @@ void attention_fwd_kernel(AttnArgs a) {  // EL: MmaBF16 or MmaF16
 #pragma unroll
                 for (int v = 0; v < 16; ++v) bm = fmaxf(bm, s[t][v]);
             bm = fmaxf(bm, __shfl_xor(bm, 32)) * a.scale_log2;
-            const float mn = fmaxf(m, bm);
+            // the running max moves only for a raise of more than the slack
+            // (from -inf, any finite or infinite block max is one)
+            const float mn = bm > m + kAttnMaxSlack ? bm : m;
             // while every key seen is masked (mn = -inf) nothing accumulates
             const float base = mn == -__builtin_inff() ? 0.0f : mn;
             const float corr = (m == mn) ? 1.0f : exp2_raw(m - base);
@@ -244,34 +267,39 @@ void attention_fwd_kernel(AttnArgs a) {  // EL: MmaBF16 or MmaF16
             }
             bs += __shfl_xor(bs, 32);
             l = l * corr + bs;
-            // rescale the accumulators only when some lane's max grew (after
-            // the first blocks it rarely does; multiplying by 1 is a no-op)
+            // rescale the accumulators only when some lane's max moved
+            // (multiplying by 1 is a no-op)
             if (__builtin_amdgcn_ballot_w64(m != mn) != 0) {
 #pragma unroll
                 for (int dt = 0; dt < kAttnD / 32; ++dt) acc[dt] *= corr;
             }
             m = mn;
 
-            // O^T += V^T P^T; V^T fragment of d-tile dt, chunk (t, c): dims
-            // dt * 32 + lane % 32, keys t * 32 + 16 c + 4 g + {0..3} and + 8,
-            // read as two 8-byte runs (pairs of keys per 32-bit word)
-            // (key chunks outer, the four independent d-tiles inner)
-            const uint16_t* vbase = &Vt[buf][(lane % 32) * kVtStride + 4 * g];
+            // O^T += V^T P^T; V^T fragment of d-tile dt, chunk ch: dims
+            // dt * 32 + lane % 32, keys 16 ch + 4 g + {0..3} and + 8 (two
+            // transposing reads; key chunks outer, the four independent
+            // d-tiles inner). Rows k0 + e have e = (k0 + e) % 4, so their
+            // swizzle is 4 e.
+            const uint16_t* vbuf = &Vs[buf][0];
 #pragma unroll
             for (int ch = 0; ch < 4; ++ch) {
-                const int k0 = (ch / 2) * 32 + (ch % 2) * 16;
+                const int k0 = ch * 16 + 4 * g;
 #pragma unroll
                 for (int dt = 0; dt < kAttnD / 32; ++dt) {
-                    const uint16_t* vrow = vbase + dt * 32 * kVtStride;
-                    const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + k0);
-                    const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + k0 + 8);
+                    const int c = dt * 4 + vt_half * 2 + vt_a / 2;  // 16-byte chunk of the run
+                    const int inner = (vt_a % 2) * 4;              // its 8-byte half
+                    const int pos = (c ^ (4 * vt_e)) * 8 + inner;
+                    const u32x2 lo = lds_read_tr16(vbuf + (k0 + vt_e) * kAttnD + pos);
+                    const u32x2 hi = lds_read_tr16(vbuf + (k0 + 8 + vt_e) * kAttnD + pos);
                     const u32x4 w = {lo.x, lo.y, hi.x, hi.y};
                     acc[dt] = EL::mfma(__builtin_bit_cast(frag, w), pf[ch], acc[dt]);
                 }
             }
         }
 
-        if (kb + 1 < nkb) store_block(buf ^ 1);
+        // this wave's loads of the next block have landed; after the barrier
+        // every wave's have, and this block's buffer is free
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();
     }
 
