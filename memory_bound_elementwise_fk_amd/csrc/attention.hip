@@ -32,8 +32,15 @@ hipError_t launch_attention_fwd(const void* q, const void* k, const void* v, voi
     a.causal = causal;
     const int64_t nwg = attention_workgroups(B, H, T);  // <= 2^23, checked by the caller
     void* args[] = {&a};
-    const void* fn = dt == kF16 ? reinterpret_cast<const void*>(&attention_fwd_kernel<MmaF16>)
-                                : reinterpret_cast<const void*>(&attention_fwd_kernel<MmaBF16>);
+    // a lane's source offsets within a 64-key block fit 32 bits unless the
+    // key strides are enormous (then the 64-bit variant)
+    const int64_t lim = (int64_t(1) << 31) - kAttnD;
+    const bool wide = a.kt > lim / kAttnBC || a.vt > lim / kAttnBC;
+    const void* fn =
+        dt == kF16 ? (wide ? reinterpret_cast<const void*>(&attention_fwd_kernel<MmaF16, true>)
+                           : reinterpret_cast<const void*>(&attention_fwd_kernel<MmaF16, false>))
+                   : (wide ? reinterpret_cast<const void*>(&attention_fwd_kernel<MmaBF16, true>)
+                           : reinterpret_cast<const void*>(&attention_fwd_kernel<MmaBF16, false>));
     return hipLaunchKernel(fn, dim3(static_cast<unsigned>(nwg)), dim3(kAttnThreads), args, 0, s);
 }
 

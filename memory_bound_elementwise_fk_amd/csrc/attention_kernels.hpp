@@ -36,6 +36,8 @@
 // so the final division by l is per lane.
 #pragma once
 
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "gemm_kernels.hpp"
 
@@ -93,7 +95,7 @@ __device__ inline u32x2 lds_read_tr16(const uint16_t* p) {
 // wave's MFMA, exponential and LDS phases run back to back and the K/V loads
 // barely overlap them; the second workgroup fills those gaps. The compiler
 // fits the kernel in 256 registers (no AGPRs, no spills) when asked to.
-template <class EL>
+template <class EL, bool WIDE>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attention_fwd_kernel(AttnArgs a) {  // EL: MmaBF16 or MmaF16
     typedef typename EL::frag frag;
@@ -151,31 +153,33 @@ void attention_fwd_kernel(AttnArgs a) {  // EL: MmaBF16 or MmaF16
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     const uint32_t ks_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((las_ptr)(&Ks[0][0])));
     const uint32_t vs_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((las_ptr)(&Vs[0][0])));
-    int64_t koff[kAttnDmaPerWave], voff[kAttnDmaPerWave];  // element offsets within a block
+    // element offsets within a block: 32-bit unless 64 rows of a stride
+    // exceed 2^31 elements (WIDE, chosen on the host)
+    typedef typename std::conditional<WIDE, int64_t, int32_t>::type off_t;
+    off_t koff[kAttnDmaPerWave], voff[kAttnDmaPerWave];
 #pragma unroll
     for (int j = 0; j < kAttnDmaPerWave; ++j) {
         const int r = (wave * kAttnDmaPerWave + j) * 4 + drow;
-        koff[j] = r * a.kt + (dpos ^ attn_swz_k(r)) * 8;
-        voff[j] = r * a.vt + (dpos ^ attn_swz_v(r)) * 8;
+        koff[j] = static_cast<off_t>(r * a.kt + (dpos ^ attn_swz_k(r)) * 8);
+        voff[j] = static_cast<off_t>(r * a.vt + (dpos ^ attn_swz_v(r)) * 8);
     }
-    auto issue_block = [&](int64_t kb0, int buf) {
+    // the block at key kb0 of K (IS_V false) or V into buffer buf
+    auto issue = [&](bool is_v, int64_t kb0, int buf) {
         const bool whole = kb0 + kAttnBC <= a.T;
-        const uint16_t* kblk = Kg + kb0 * a.kt;
-        const uint16_t* vblk = Vg + kb0 * a.vt;
+        const uint16_t* base = is_v ? Vg : Kg;
+        const int64_t st = is_v ? a.vt : a.kt;
+        const uint16_t* blk = base + kb0 * st;
+        const uint32_t lds = (is_v ? vs_base : ks_base) + static_cast<uint32_t>(buf * kAttnBlockBytes);
 #pragma unroll
         for (int j = 0; j < kAttnDmaPerWave; ++j) {
-            const uint32_t off = static_cast<uint32_t>(
-                buf * kAttnBlockBytes + (wave_s * kAttnDmaPerWave + j) * 1024);
-            const uint16_t* ksrc = kblk + koff[j];
-            const uint16_t* vsrc = vblk + voff[j];
+            const uint32_t off = static_cast<uint32_t>((wave_s * kAttnDmaPerWave + j) * 1024);
+            const uint16_t* src = blk + (is_v ? voff[j] : koff[j]);
             if (!whole) {
                 const int r = (wave * kAttnDmaPerWave + j) * 4 + drow;
                 const int64_t key = kb0 + r < a.T ? kb0 + r : a.T - 1;
-                ksrc = Kg + key * a.kt + (dpos ^ attn_swz_k(r)) * 8;
-                vsrc = Vg + key * a.vt + (dpos ^ attn_swz_v(r)) * 8;
+                src = base + key * st + (dpos ^ (is_v ? attn_swz_v(r) : attn_swz_k(r))) * 8;
             }
-            lds_dma16(ksrc, ks_base + off);
-            lds_dma16(vsrc, vs_base + off);
+            lds_dma16(src, lds + off);
         }
     };
 
@@ -191,34 +195,48 @@ void attention_fwd_kernel(AttnArgs a) {  // EL: MmaBF16 or MmaF16
     // a = lane % 4, half = (lane / 16) % 2
     const int vt_e = (lane % 16) / 4, vt_a = lane % 4, vt_half = (lane / 16) % 2;
 
-    issue_block(0, 0);
+    // S^T of one 64-key block from K buffer kbuf: the block's two 32-key
+    // tiles alternate so that consecutive MFMAs are independent (a lone tile
+    // is a chain of 8 dependent MFMAs, each also waiting on its LDS read)
+    const int kr = lane % 32;  // + t * 32: the same swizzle (r % 16)
+    auto compute_s = [&](int kbuf, f32x16 (&s)[2]) {
+        s[0] = f32x16{};
+        s[1] = f32x16{};
+        const uint16_t* kbase = &Ks[kbuf][kr * kAttnD];
+#pragma unroll
+        for (int kk = 0; kk < kAttnD / 16; ++kk)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                s[t] = EL::mfma(*reinterpret_cast<const frag*>(
+                                    kbase + t * 32 * kAttnD + (((2 * kk + g) ^ attn_swz_k(kr)) * 8)),
+                                qf[kk], s[t]);
+    };
+    // a causal block wholly above this wave's queries contributes nothing
+    // (its last key block can be): the wave skips it (uniform branch)
+    auto wave_needs = [&](int64_t kbx) { return !(a.causal && kbx * kAttnBC > q0 + 31); };
+
+    // Software pipeline: block kb's softmax (VALU) runs next to block
+    // kb + 1's S^T MFMAs, so K is loaded two blocks ahead and V one: in
+    // iteration kb, K(kb + 2) goes to the K buffer K(kb) left (read for S(kb)
+    // an iteration earlier) and V(kb + 1) to the one V(kb - 1) left. One
+    // barrier per iteration, after every wave's loads have landed.
+    issue(false, 0, 0);
+    issue(true, 0, 0);
+    if (nkb > 1) issue(false, kAttnBC, 1);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
+    f32x16 s_cur[2] = {f32x16{}, f32x16{}};
+    if (wave_needs(0)) compute_s(0, s_cur);
+    __syncthreads();  // every wave has read K(0) before K(2) replaces it
     for (int64_t kb = 0; kb < nkb; ++kb) {
-        const int buf = static_cast<int>(kb & 1);
         const int64_t kb0 = kb * kAttnBC;
-        // the other buffer was last read in the previous block, which every
-        // wave has left (the barrier at its end)
-        if (kb + 1 < nkb) issue_block(kb0 + kAttnBC, buf ^ 1);
-
-        // a causal block wholly above this wave's queries contributes nothing
-        // (its last key block can be): the wave skips it (uniform branch)
-        if (!(a.causal && kb0 > q0 + 31)) {
-            // S^T for the block's two 32-key tiles; the tiles alternate so
-            // that consecutive MFMAs are independent (a lone tile is a chain
-            // of 8 dependent MFMAs, each also waiting on its LDS read)
-            f32x16 s[2] = {f32x16{}, f32x16{}};
-            const int kr = lane % 32;  // + t * 32: the same swizzle (r % 16)
-            const uint16_t* kbase = &Ks[buf][kr * kAttnD];
-#pragma unroll
-            for (int kk = 0; kk < kAttnD / 16; ++kk)
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-                    s[t] = EL::mfma(*reinterpret_cast<const frag*>(
-                                        kbase + t * 32 * kAttnD +
-                                        (((2 * kk + g) ^ attn_swz_k(kr)) * 8)),
-                                    qf[kk], s[t]);
-
+        if (kb + 2 < nkb) issue(false, kb0 + 2 * kAttnBC, static_cast<int>(kb & 1));
+        if (kb + 1 < nkb) issue(true, kb0 + kAttnBC, static_cast<int>((kb + 1) & 1));
+        // S(kb + 1); in the last iteration it reads a stale buffer (valid
+        // LDS) and is discarded, which keeps the MFMAs next to the softmax
+        f32x16 s_nxt[2];
+        if (wave_needs(kb)) {
+            f32x16 (&s)[2] = s_cur;
             // mask (only blocks that reach past T or, causal, past the wave's
             // first query), then the block max over the query's 32 keys, in
             // raw score units (the scale is positive)
@@ -232,6 +250,7 @@ void attention_fwd_kernel(AttnArgs a) {  // EL: MmaBF16 or MmaF16
                     }
                 }
             }
+            compute_s(static_cast<int>((kb + 1) & 1), s_nxt);
             float bm = -__builtin_inff();
 #pragma unroll
             for (int t = 0; t < 2; ++t)
@@ -280,7 +299,7 @@ void attention_fwd_kernel(AttnArgs a) {  // EL: MmaBF16 or MmaF16
             // transposing reads; key chunks outer, the four independent
             // d-tiles inner). Rows k0 + e have e = (k0 + e) % 4, so their
             // swizzle is 4 e.
-            const uint16_t* vbuf = &Vs[buf][0];
+            const uint16_t* vbuf = &Vs[kb & 1][0];
 #pragma unroll
             for (int ch = 0; ch < 4; ++ch) {
                 const int k0 = ch * 16 + 4 * g;
@@ -295,10 +314,14 @@ void attention_fwd_kernel(AttnArgs a) {  // EL: MmaBF16 or MmaF16
                     acc[dt] = EL::mfma(__builtin_bit_cast(frag, w), pf[ch], acc[dt]);
                 }
             }
+        } else {
+            compute_s(static_cast<int>((kb + 1) & 1), s_nxt);
         }
+        s_cur[0] = s_nxt[0];
+        s_cur[1] = s_nxt[1];
 
-        // this wave's loads of the next block have landed; after the barrier
-        // every wave's have, and this block's buffer is free
+        // this wave's loads have landed; after the barrier every wave's
+        // have, and the buffers read in this iteration are free
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();
     }
