@@ -151,3 +151,27 @@ def test_attention_fp16_strided_and_closed_form():
     # row 0 under the causal mask is V[0] exactly
     q, k, v = qkv(1, 2, 77, seed=4, dt="fp16")
     assert np.array_equal(run(q, k, v, True)[:, :, 0], v[:, :, 0])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_wide_key_strides(causal):
+    # K and V rows 2^25 + 8 elements apart: 64 rows of that stride pass 2^31
+    # elements, so the kernel takes its 64-bit load-offset variant; T = 66 is
+    # one whole 64-key block and a partial one (about 4.4 GB per operand)
+    B, H, T, d = 1, 1, 66, 128
+    stride = (1 << 25) + 8
+    q, k, v = qkv(B, H, T, seed=23)
+    span = (T - 1) * stride + d
+    views = []
+    for a in (k, v):
+        buf = torch.empty(span, dtype=torch.bfloat16, device=DEV)
+        view = buf.as_strided((B, H, T, d), (T * stride, T * stride, stride, 1))
+        view.copy_(to_dev(a))
+        views.append(view)
+    o = torch.empty((B, H, T, d), dtype=torch.bfloat16, device=DEV)
+    fk.fk_attention_fwd(to_dev(q), views[0], views[1], o, causal=causal)
+    got = to_host(o)
+    ref = oracle.attention(q, k, v, causal=causal)
+    check_rows({(0, 0): got[0, 0]}, {(0, 0): ref[0, 0]}, v, f"wide strides causal={causal}")
+    del views
+    torch.cuda.empty_cache()
