@@ -11,6 +11,7 @@ streams. ``y`` is written in place (``y`` may be ``x`` itself).
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 from pathlib import Path
 
@@ -141,6 +142,15 @@ def _device_tensor(t, name: str):
         raise ValueError(f"{name} must be a GPU tensor, got device {t.device}")
 
 
+def _on_device(t):
+    """Context making t's GPU current for the call: a no-op when it already
+    is (entering torch.cuda.device costs a few microseconds per call)."""
+    torch = _torch()
+    if t.device.index is None or t.device.index == torch.cuda.current_device():
+        return contextlib.nullcontext()
+    return torch.cuda.device(t.device)
+
+
 def _stream_handle(t, stream) -> int | None:
     if stream is None:
         return _torch().cuda.current_stream(t.device).cuda_stream
@@ -196,7 +206,7 @@ def _rows_pair(x, y, what: str):
 def fk_gelu_tanh(x, y, stream=None) -> None:
     """y = tanh-GELU(x) elementwise (fp32 or bf16, contiguous, same size)."""
     n, dt = _flat_pair(x, y, "fk_gelu_tanh")
-    with _torch().cuda.device(x.device):
+    with _on_device(x):
         _check(lib().fk_gelu_tanh(x.data_ptr(), y.data_ptr(), n, dt, _stream_handle(x, stream)),
                "fk_gelu_tanh")
 
@@ -205,7 +215,7 @@ def fk_elementwise_chain(x, y, ops, stream=None) -> None:
     """y = ops applied in order to x; ops is a sequence of (kind, scalar)."""
     n, dt = _flat_pair(x, y, "fk_elementwise_chain")
     arr, count = _ops_array(ops)
-    with _torch().cuda.device(x.device):
+    with _on_device(x):
         _check(lib().fk_elementwise_chain(x.data_ptr(), y.data_ptr(), n, dt, arr, count,
                                           _stream_handle(x, stream)), "fk_elementwise_chain")
 
@@ -213,7 +223,7 @@ def fk_elementwise_chain(x, y, ops, stream=None) -> None:
 def fk_softmax_rows(x, y, stream=None) -> None:
     """Softmax along each row of a 2-D x into y (row strides honoured)."""
     rows, cols, ldx, ldy, dt = _rows_pair(x, y, "fk_softmax_rows")
-    with _torch().cuda.device(x.device):
+    with _on_device(x):
         _check(lib().fk_softmax_rows(x.data_ptr(), y.data_ptr(), rows, cols, ldx, ldy, dt,
                                      _stream_handle(x, stream)), "fk_softmax_rows")
 
@@ -221,7 +231,7 @@ def fk_softmax_rows(x, y, stream=None) -> None:
 def fk_softmax_rows_online(x, y, stream=None) -> None:
     """As fk_softmax_rows, always through the online two-pass kernel."""
     rows, cols, ldx, ldy, dt = _rows_pair(x, y, "fk_softmax_rows_online")
-    with _torch().cuda.device(x.device):
+    with _on_device(x):
         _check(lib().fk_softmax_rows_online(x.data_ptr(), y.data_ptr(), rows, cols, ldx, ldy, dt,
                                             _stream_handle(x, stream)), "fk_softmax_rows_online")
 
@@ -235,7 +245,7 @@ def fk_softmax_rows_ws(x, y, workspace, stream=None) -> None:
     else:
         _device_tensor(workspace, "workspace")
         wptr, wbytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    with _torch().cuda.device(x.device):
+    with _on_device(x):
         _check(lib().fk_softmax_rows_ws(x.data_ptr(), y.data_ptr(), rows, cols, ldx, ldy, dt,
                                         wptr, wbytes, _stream_handle(x, stream)),
                "fk_softmax_rows_ws")
@@ -290,7 +300,7 @@ def fk_layernorm_rows(x, y, gamma=None, beta=None, eps: float = 1e-5, gelu: bool
     """LayerNorm along each row of a 2-D x into y (optionally then tanh-GELU)."""
     rows, cols, ldx, ldy, dt = _rows_pair(x, y, "fk_layernorm_rows")
     g, b = _param(gamma, x, "gamma"), _param(beta, x, "beta")
-    with _torch().cuda.device(x.device):
+    with _on_device(x):
         _check(lib().fk_layernorm_rows(x.data_ptr(), y.data_ptr(), rows, cols, ldx, ldy, g, b,
                                        float(eps), int(bool(gelu)), dt, _stream_handle(x, stream)),
                "fk_layernorm_rows")
@@ -308,7 +318,7 @@ def fk_gelu_tanh_backward(x, dy, dx, stream=None) -> None:
     """dx = dy * GELU'(x) elementwise (fp32 or bf16, contiguous, same size)."""
     n, dt = _flat_pair(x, dx, "fk_gelu_tanh_backward")
     _flat_pair(dy, dx, "fk_gelu_tanh_backward")
-    with _torch().cuda.device(x.device):
+    with _on_device(x):
         _check(lib().fk_gelu_tanh_backward(x.data_ptr(), dy.data_ptr(), dx.data_ptr(), n, dt,
                                            _stream_handle(x, stream)), "fk_gelu_tanh_backward")
 
@@ -317,7 +327,7 @@ def fk_softmax_rows_backward(y, dy, dx, stream=None) -> None:
     """dx = y * (dy - sum(y * dy)) per row of 2-D y, dy into dx (row strides honoured)."""
     rows, cols, ldy, lddx, dt = _rows_pair(y, dx, "fk_softmax_rows_backward")
     _, _, lddy, _, _ = _rows_pair(dy, dx, "fk_softmax_rows_backward")
-    with _torch().cuda.device(y.device):
+    with _on_device(y):
         _check(lib().fk_softmax_rows_backward(y.data_ptr(), dy.data_ptr(), dx.data_ptr(), rows,
                                               cols, ldy, lddy, lddx, dt,
                                               _stream_handle(y, stream)),
@@ -361,7 +371,7 @@ def fk_linear_gelu(x, w, bias, y, gelu: bool = True, stream=None, activation: st
     else:
         raise ValueError(f"fk_linear_gelu: activation must be one of {sorted(_ACTS)}")
     ld = lambda t, n: t.stride(0) if t.shape[0] > 1 else n  # noqa: E731
-    with _torch().cuda.device(x.device):
+    with _on_device(x):
         _check(lib().fk_linear_gelu(x.data_ptr(), w.data_ptr(), b, y.data_ptr(), M, N, K,
                                     ld(x, K), ld(w, K), ld(y, N), act,
                                     _dtype_code(x), _stream_handle(x, stream)), "fk_linear_gelu")
@@ -380,7 +390,7 @@ def fk_attention_fwd(q, k, v, o, causal: bool = True, stream=None) -> None:
             raise TypeError("fk_attention_fwd: q, k, v, o must share a dtype")
     B, H, T, d = q.shape
     st = (ctypes.c_int64 * 12)(*[int(t.stride(i)) for t in (q, k, v, o) for i in range(3)])
-    with _torch().cuda.device(q.device):
+    with _on_device(q):
         _check(lib().fk_attention_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B,
                                       H, T, d, st, int(bool(causal)), _dtype_code(q),
                                       _stream_handle(q, stream)), "fk_attention_fwd")
@@ -394,7 +404,7 @@ def fk_copy(x, y, nbytes: int | None = None, stream=None) -> None:
         nbytes = x.numel() * x.element_size()
     if nbytes > x.numel() * x.element_size() or nbytes > y.numel() * y.element_size():
         raise ValueError("fk_copy: nbytes exceeds a buffer")
-    with _torch().cuda.device(x.device):
+    with _on_device(x):
         _check(lib().fk_copy(x.data_ptr(), y.data_ptr(), nbytes, _stream_handle(x, stream)),
                "fk_copy")
 
