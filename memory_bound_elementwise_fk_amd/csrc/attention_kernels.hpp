@@ -10,11 +10,11 @@
 // the end. As on that page, P is rounded to the input dtype before the
 // P V product. The causal mask keeps key j for query i when j <= i.
 //
-// MI355X mapping. Each wave owns 32 queries; a workgroup of W waves owns
-// 32 W queries of one (batch, head) and walks the key blocks of 64 keys,
-// staged through LDS (K and V both as [key][dim], double-buffered, copied
-// one block ahead by direct global-to-LDS loads: no registers, no ALU). The
-// wave
+// MI355X mapping. Each wave owns 32 queries; a workgroup of 4 waves owns
+// 128 queries of one (batch, head) and walks the key blocks of 64 keys,
+// staged through LDS (K and V both as [key][dim], two buffers each, copied
+// by direct global-to-LDS loads: no registers, no ALU; K two blocks ahead,
+// V one, for the software pipeline described at the loop). The wave
 // computes the transposed scores S^T = K Q^T with the 32x32x16 bf16 MFMA:
 // K is the A operand (lane l: key l % 32, dims (l / 32) * 8 + e), Q the B
 // operand (query l % 32), held in registers for the whole key loop. In the
@@ -94,7 +94,8 @@ __device__ inline u32x2 lds_read_tr16(const uint16_t* p) {
 // Two waves per SIMD (two workgroups per CU; LDS 70 KiB each): with one, a
 // wave's MFMA, exponential and LDS phases run back to back and the K/V loads
 // barely overlap them; the second workgroup fills those gaps. The compiler
-// fits the kernel in 256 registers (no AGPRs, no spills) when asked to.
+// fits the kernel in 256 registers (no AGPRs) when asked to, spilling a few
+// load offsets that are reloaded outside the MFMA phases.
 template <class EL, bool WIDE>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attention_fwd_kernel(AttnArgs a) {  // EL: MmaBF16 or MmaF16
