@@ -15,8 +15,10 @@ wall time between two device synchronisations, in GB/s (1e9 B/s).
 
 Per-kernel durations come from HIP events recorded on the launch stream
 around every launch of K further steps (not the timed ones: the events
-would add to the step). The CPU baseline repeats the oracle over whole
-steps on the host's cores for at least 10 s.
+would add to the step). Each kernel is also set against a plain copy of
+its own bytes (``copy_same_bytes_ms``, ``frac_of_copy``), timed the same way
+in K steps of copies: a copy's rate depends on its size. The CPU baseline
+repeats the oracle over whole steps on the host's cores for at least 10 s.
 
 Prints ONE JSON line. ``--gpus`` above 1 is refused: the build measures one
 GPU.
@@ -181,6 +183,17 @@ def main() -> int:
     spot = spot_check(host, ys, wl)
     log(f"spot check: {spot}")
 
+    # ---- each kernel's own ceiling: K more steps in which every kernel is
+    # replaced by a plain 16-byte copy of its bytes (its input read once, the
+    # same number of bytes written), timed the same way. A copy's rate depends
+    # on its size (a short one pays its launch and pipeline fill), so each
+    # kernel is set against the copy of equal size; this overwrites the
+    # outputs, which is why it runs after the spot check
+    copy_ms = copy_steps(fk, torch, xs, ys, stream, args.steps)
+    for name in STEP:
+        kernels[name]["copy_same_bytes_ms"] = round(copy_ms[name], 5)
+        kernels[name]["frac_of_copy"] = round(copy_ms[name] / per_kernel_ms[name], 4)
+
     extras = {}
     if not args.no_extras:
         extras = measure_extras(fk, wl, torch, xs, ys, stream)
@@ -222,6 +235,23 @@ def main() -> int:
     }
     print(json.dumps(result), flush=True)
     return 0 if spot["ok"] else 1
+
+
+def copy_steps(fk, torch, xs, ys, stream, steps):
+    """Average duration of a copy of each step kernel's input (x to y, all of
+    x's bytes), over `steps` steps with HIP events around every launch."""
+    ev = {name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(steps)] for name in STEP}
+    for k in range(-1, steps):  # step -1: warmup
+        for name in STEP:
+            x, y = xs[name], ys[name]
+            if k >= 0:
+                ev[name][k][0].record(stream)
+            fk.fk_copy(x, y, x.numel() * x.element_size())
+            if k >= 0:
+                ev[name][k][1].record(stream)
+    torch.cuda.synchronize()
+    return {name: sum(a.elapsed_time(b) for a, b in ev[name]) / steps for name in STEP}
 
 
 def spot_check(host, ys, wl):
