@@ -1,8 +1,8 @@
 """GPU parity of the FlashAttention forward kernel against the CPU oracle.
 Needs an MI355X.
 
-Tolerance (derived from the kernel's arithmetic; the pages and the north
-star fix none for attention): |o - r| <= ulp_bf16(|r|) + 2^-8 max|v| per
+Tolerance (derived from the kernel's arithmetic; none is stated for
+attention): |o - r| <= ulp_bf16(|r|) + 2^-8 max|v| per
 (batch, head). O = sum_j p_j v_j / l. The kernel rounds p_j to bf16 before
 the P V product (as the page's kernel rounds P to V's dtype): relative error
 <= 2^-9 per weight, so at most 2^-9 max|v| after the division by l (the sum

@@ -1,8 +1,8 @@
 """GPU parity of the Linear + GELU kernel (MFMA) against the CPU oracle.
 Needs an MI355X.
 
-Tolerance (derived from the arithmetic; the pages and the benchmark spec fix
-none for the matmul): the kernel accumulates the K products in fp32 in an
+Tolerance (derived from the arithmetic; none is stated for the
+matmul): the kernel accumulates the K products in fp32 in an
 order the matrix cores choose, so any summation order must pass:
 |y - r| <= ulp_bf16(|r|) + 1.13 (K + 2) 2^-24 ((|x| |w|^T)_ij + |b_j|)
 (the rounding of y to bf16, plus the worst-case fp32 accumulation error,
