@@ -205,6 +205,34 @@ def test_chain_relu_is_bit_exact(dt):
     assert np.array_equal(got.view(bits), ref.view(bits))
 
 
+# The last, ragged tile runs other code than the full tiles (whole vectors
+# under a mask, then the < 16-byte tail one element per lane): the same
+# inputs must give the same bits there as in the first, full tile.
+# Workgroup tiles: fp32 64 lanes x 4 = 256 elements, bf16 128 lanes x 8 = 1024.
+@pytest.mark.parametrize("dt,n", [("f32", 3 * 256 + 5 * 4 + 3), ("f32", 256 + 1),
+                                  ("bf16", 3 * 1024 + 5 * 8 + 7), ("bf16", 1024 + 3)])
+@pytest.mark.parametrize("op", ["gelu", "chain"])
+def test_ragged_tile_matches_full_tile_bitwise(dt, n, op):
+    tile = 256 if dt == "f32" else 1024
+    rest = n % tile  # elements in the ragged tile
+    specials = np.array([0.0, -0.0, 1.0, -1.0, 6.0, -3.0, -9.7, -30.0, 1e-30, np.inf, -np.inf,
+                         np.nan], dtype=np.float32)
+    xf = (np.random.default_rng(n).standard_normal(n) * 3.0).astype(np.float32)
+    xf[:len(specials)] = specials
+    xf[n - rest:] = xf[:rest]  # the ragged tile repeats the start of the first tile
+    x = xf if dt == "f32" else wl.f32_to_bf16_bits(xf)
+    xt = to_dev(x)
+    full, y = guarded(x.shape, tdtype(dt))
+    if op == "gelu":
+        fk.fk_gelu_tanh(xt, y)
+    else:
+        fk.fk_elementwise_chain(xt, y, C3)
+    got = to_host(y)
+    assert guards_intact(full, n), f"{op} wrote outside its output"
+    bits = got.view(np.uint32 if dt == "f32" else np.uint16)
+    assert np.array_equal(bits[n - rest:], bits[:rest]), f"{op} {dt} n={n}: ragged tile differs"
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("n", [1, 7, 4097, 50_001])
 def test_chain_long_op_lists(dt, n):
