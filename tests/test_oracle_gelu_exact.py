@@ -15,21 +15,21 @@ doubles), and exp(-2u) turns that into |2u| times as much, so the bound used
 is |r - e| <= (8 |u(x)| + 8) 2^-53 |e| (|u| = 71 at x = -12: about 6e-14;
 a wrong constant or a dropped term is off by 1e-3 or more).
 """
-from decimal import Decimal, getcontext
+from decimal import Decimal, localcontext
 
 import numpy as np
 
 import oracle
 
-getcontext().prec = 150
+PREC = 150  # digits; every evaluation runs in a local context of this precision
 
 
 def _atan_inv(n: int) -> Decimal:
-    """atan(1/n) by its Taylor series (n >= 2)."""
+    """atan(1/n) by its Taylor series (n >= 2), in the current context."""
     x = Decimal(1) / n
     x2 = x * x
     term, total, k = x, x, 1
-    eps = Decimal(10) ** (-getcontext().prec - 5)
+    eps = Decimal(10) ** (-PREC - 10)
     while True:
         term *= -x2
         k += 2
@@ -39,8 +39,10 @@ def _atan_inv(n: int) -> Decimal:
         total += d
 
 
-PI = 16 * _atan_inv(5) - 4 * _atan_inv(239)  # Machin
-C = (Decimal(2) / PI).sqrt()
+with localcontext() as _ctx:
+    _ctx.prec = PREC + 10
+    PI = 16 * _atan_inv(5) - 4 * _atan_inv(239)  # Machin
+    C = (Decimal(2) / PI).sqrt()
 A = Decimal("0.044715")
 
 
@@ -50,18 +52,22 @@ def _tanh(u: Decimal) -> Decimal:
 
 
 def gelu_exact(x: float) -> Decimal:
-    X = Decimal(x)  # the double's exact value
-    u = C * (X + A * X ** 3)
-    return Decimal("0.5") * X * (1 + _tanh(u))
+    with localcontext() as ctx:
+        ctx.prec = PREC
+        X = Decimal(x)  # the double's exact value
+        u = C * (X + A * X ** 3)
+        return Decimal("0.5") * X * (1 + _tanh(u))
 
 
 def gelu_grad_exact(x: float) -> Decimal:
     """d/dx of the literal expression: 0.5 (1 + tanh u) + 0.5 x (1 - tanh^2 u) u'."""
-    X = Decimal(x)
-    u = C * (X + A * X ** 3)
-    du = C * (1 + 3 * A * X ** 2)
-    t = _tanh(u)
-    return Decimal("0.5") * (1 + t) + Decimal("0.5") * X * (1 - t * t) * du
+    with localcontext() as ctx:
+        ctx.prec = PREC
+        X = Decimal(x)
+        u = C * (X + A * X ** 3)
+        du = C * (1 + 3 * A * X ** 2)
+        t = _tanh(u)
+        return Decimal("0.5") * (1 + t) + Decimal("0.5") * X * (1 - t * t) * du
 
 
 def _u(x):

@@ -10,22 +10,21 @@ once to fp32, so its results lie within one fp32 ulp of the exact values
 (half an ulp from the final rounding, a little more from the double
 arithmetic), and almost all are the exact value correctly rounded.
 """
-from decimal import Decimal, getcontext
+from decimal import Decimal, localcontext
 
 import numpy as np
 
 import oracle
 from memory_bound_elementwise_fk_amd import workloads as wl
 
-getcontext().prec = 60
-
-
 def softmax_exact(row) -> list:
-    xs = [Decimal(float(v)) for v in row]
-    m = max(xs)
-    es = [(v - m).exp() for v in xs]
-    s = sum(es)
-    return [e / s for e in es]
+    with localcontext() as ctx:
+        ctx.prec = 60
+        xs = [Decimal(float(v)) for v in row]
+        m = max(xs)
+        es = [(v - m).exp() for v in xs]
+        s = sum(es)
+        return [e / s for e in es]
 
 
 def _round_f32(d: Decimal) -> np.float32:
