@@ -29,8 +29,9 @@
 //    formula; the standard definition over the last axis is used: mean, the
 //    biased variance, (x - mean) / sqrt(var + eps), then gamma and beta per
 //    column, optionally followed by the tanh-GELU above.
-//  * Backward (the pages print no formulas; the P2 page names autograd
-//    integration as later work): derived from the forward definitions above.
+//  * Backward (the pages print no formulas; the Triton tutorial page,
+//    accesspath.com "Triton in practice", names autograd integration as
+//    later work): derived from the forward definitions above.
 //    GELU'(x) = s + 2 x k (1 + 3 c x^2) s (1 - s), s = 1 / (1 + e^(-2u)),
 //    k = sqrt(2/pi), c = 0.044715, with 1 - s evaluated as 1 / (1 + e^(2u));
 //    dx = dy * GELU'(x). Softmax: dx_j = y_j (dy_j - sum_k y_k dy_k), the
@@ -43,7 +44,8 @@
 //    (what the formula gives).
 //
 // Pins: tests/test_oracle_*.py check this file against torch's and scipy's
-// own routines, closed-form identities and the pages' worked example.
+// own routines, the definitions evaluated exactly in high-precision decimal
+// arithmetic, closed-form identities and the pages' worked example.
 
 #include <cmath>
 #include <cstdint>
