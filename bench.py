@@ -190,6 +190,9 @@ def main() -> int:
     # kernel is set against the copy of equal size; this overwrites the
     # outputs, which is why it runs after the spot check
     copy_ms = copy_steps(fk, torch, xs, ys, stream, args.steps)
+    for name in STEP:  # the step's outputs again (the extras reuse them)
+        launches[name]()
+    torch.cuda.synchronize()
     for name in STEP:
         kernels[name]["copy_same_bytes_ms"] = round(copy_ms[name], 5)
         kernels[name]["frac_of_copy"] = round(copy_ms[name] / per_kernel_ms[name], 4)
