@@ -30,7 +30,9 @@
  *   nothing; pointers may then be NULL.
  * Errors: invalid arguments return a negative fk_status BEFORE any HIP call
  *   and nothing is launched. A failed launch returns FK_ERR_HIP.
- * Threads: entry points keep no state and may be called concurrently.
+ * Threads: entry points keep no per-call state and may be called
+ *   concurrently; the one process-wide setting is the wait bound of
+ *   fk_set_split_wait_limit.
  */
 #ifndef FUSEDOPS_H
 #define FUSEDOPS_H
@@ -47,7 +49,11 @@ typedef enum {
     FK_OK = 0,
     FK_ERR_INVALID_ARG = -1, /* null pointer with work to do, negative size,
                                 stride < cols, unknown dtype, bad op list   */
-    FK_ERR_UNSUPPORTED = -2, /* a size beyond what one launch can address   */
+    FK_ERR_UNSUPPORTED = -2, /* valid but not handled here: a size beyond
+                                what one launch can address, a row wider
+                                than the entry point's capacity, FK_F16
+                                outside Linear and attention, an attention
+                                head dimension other than 128               */
     FK_ERR_OVERLAP = -3,     /* input and output overlap without being equal */
     FK_ERR_HIP = -4          /* the HIP runtime reported an error           */
 } fk_status;
