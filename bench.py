@@ -49,7 +49,16 @@ KERNEL_NAMES = {
     "C5a": ("softmax_split_kernel<fk::IoF32",),
     "C5b": ("ew_vec_kernel<fk::IoBF16", "GeluOp"),
     "copy": ("copy_vec_kernel",),
+    "layernorm_gelu": ("layernorm_reg_kernel<fk::IoBF16",),
+    "gelu_backward": ("ew2_vec_kernel<fk::IoBF16", "GeluBwdOp"),
+    "softmax_backward": ("softmax_bwd_reg_kernel<fk::IoBF16",),
 }
+# Next-row kernels in the counter run (bytes per launch: one read of each
+# input, one write of the output; gamma and beta of the LayerNorm once).
+EXTRA = ("layernorm_gelu", "gelu_backward", "softmax_backward")
+EXTRA_BYTES = {"layernorm_gelu": 2 * 32768 * 4096 * 2 + 2 * 4096 * 2,
+               "gelu_backward": 3 * (1 << 30) * 2,
+               "softmax_backward": 3 * 32768 * 4096 * 2}
 CPU_BASELINE_MIN_SECONDS = 10.0
 
 
@@ -568,7 +577,9 @@ def cpu_baseline(host, kbytes):
 
 
 def counters_run(fk, torch, launches, xs, ys):
-    """Each step kernel twice and one 1 GiB copy, for per-dispatch counters."""
+    """Each step kernel twice and one 1 GiB copy, for per-dispatch counters;
+    then twice each of the LayerNorm + GELU, GELU backward and softmax
+    backward launches the extras time (same shapes)."""
     calib = 1 << 30
     a = torch.empty(calib, dtype=torch.uint8, device="cuda:0")
     b = torch.empty_like(a)
@@ -577,8 +588,41 @@ def counters_run(fk, torch, launches, xs, ys):
         for name in STEP:
             launches[name]()
     torch.cuda.synchronize()
-    log(f"counters run done: calibration copy {calib} B, then 2 x {', '.join(STEP)}")
+    del a, b
+    extra = extra_launches(fk, torch, xs, ys)
+    for _ in range(2):
+        for name in EXTRA:
+            extra[name]()
+    torch.cuda.synchronize()
+    log(f"counters run done: calibration copy {calib} B, then 2 x {', '.join(STEP)}, "
+        f"then 2 x {', '.join(EXTRA)}")
     return 0
+
+
+def extra_launches(fk, torch, xs, ys):
+    """The memory-bound next-row kernels on the extras' shapes: LayerNorm +
+    GELU bf16 32768 x 4096 (random gamma, beta), GELU backward over the C5b
+    tensor (dy: the step's GELU output), softmax backward on the C4 shape
+    (y: the step's softmax output, dy: the C4 input)."""
+    import numpy as np
+
+    from memory_bound_elementwise_fk_amd import workloads as wl
+
+    xb = wl.to_torch(wl.draw(32768 * 4096, seed=0, scale=8.0, dtype="bf16"),
+                     "cuda:0").view(32768, 4096)
+    prng = np.random.default_rng(8)
+    gb = wl.to_torch(wl.f32_to_bf16_bits(
+        (1.0 + 0.25 * prng.standard_normal(4096)).astype(np.float32)), "cuda:0")
+    bb = wl.to_torch(wl.f32_to_bf16_bits(
+        (0.5 * prng.standard_normal(4096)).astype(np.float32)), "cuda:0")
+    yb = torch.empty_like(xb)
+    dx5 = torch.empty_like(xs["C5b"])
+    dx4 = torch.empty_like(ys["C4"])
+    return {
+        "layernorm_gelu": lambda: fk.fk_layernorm_rows(xb, yb, gb, bb, gelu=True),
+        "gelu_backward": lambda: fk.fk_gelu_tanh_backward(xs["C5b"], ys["C5b"], dx5),
+        "softmax_backward": lambda: fk.fk_softmax_rows_backward(ys["C4"], xs["C4"], dx4),
+    }
 
 
 def _read_counter_csv(path):
@@ -640,6 +684,19 @@ def ingest_counters(fetch_csv: str, write_csv: str) -> int:
                                 "bytes_per_launch": round(fb + wb), "algorithmic_bytes": alg,
                                 "ratio_to_algorithmic": round((fb + wb) / alg, 4),
                                 "dispatches": len(fv)}
+    # the next-row kernels, when the run counted them
+    for name in EXTRA:
+        fv = per_kernel(fetch, KERNEL_NAMES[name])
+        wv = per_kernel(write, KERNEL_NAMES[name])
+        if not fv or not wv:
+            continue
+        fb = sum(fv) / len(fv) * 1024.0 * f_scale
+        wb = sum(wv) / len(wv) * 1024.0 * w_scale
+        alg = EXTRA_BYTES[name]
+        rec.setdefault("next_rows", {})[name] = {
+            "fetch_bytes": round(fb), "write_bytes": round(wb), "bytes_per_launch": round(fb + wb),
+            "algorithmic_bytes": alg, "ratio_to_algorithmic": round((fb + wb) / alg, 4),
+            "dispatches": len(fv)}
     TRAFFIC_FILE.parent.mkdir(exist_ok=True)
     TRAFFIC_FILE.write_text(json.dumps(rec, indent=2) + "\n")
     print(json.dumps(rec, indent=2))

@@ -34,6 +34,9 @@ NAMES = {
     "C4": "void fk::softmax_reg_kernel<fk::IoBF16, 2, 4, true, true, 2>(...)",
     "C5a": "void fk::softmax_split_kernel<fk::IoF32, 256, 8, true, true>(...)",
     "C5b": "void fk::ew_vec_kernel<fk::IoBF16, 128, 1, true, false, fk::GeluOp>(...)",
+    "layernorm_gelu": "void fk::layernorm_reg_kernel<fk::IoBF16, 4, 2, true, true, true, 2>(...)",
+    "gelu_backward": "void fk::ew2_vec_kernel<fk::IoBF16, 128, true, false, fk::GeluBwdOp>(...)",
+    "softmax_backward": "void fk::softmax_bwd_reg_kernel<fk::IoBF16, 2, 4, true, true, 2>(...)",
 }
 
 
@@ -61,6 +64,17 @@ def test_ingest_counters_scales_by_the_calibration_copy(tmp_path, monkeypatch):
             fetch.append((d, NAMES[name], half / 1024 / 2))
             write.append((d, NAMES[name], half / 1024))
             d += 1
+    # the next-row kernels: reads of every input, one write (LayerNorm: x and
+    # gamma/beta read, y written)
+    for _ in range(2):
+        for name in bench.EXTRA:
+            total = bench.EXTRA_BYTES[name]
+            written = 2 * 32768 * 4096 if name != "gelu_backward" else 2 * (1 << 30)
+            if name == "layernorm_gelu":
+                written = 32768 * 4096 * 2
+            fetch.append((d, NAMES[name], (total - written) / 1024 / 2))
+            write.append((d, NAMES[name], written / 1024))
+            d += 1
     # a counter split over two rows of one dispatch (several agents/XCDs) is summed
     fetch[1] = (fetch[1][0], fetch[1][1], fetch[1][2] / 2)
     fetch.insert(2, fetch[1])
@@ -75,6 +89,11 @@ def test_ingest_counters_scales_by_the_calibration_copy(tmp_path, monkeypatch):
     for name in bench.STEP:
         k = rec["kernels"][name]
         assert k["bytes_per_launch"] == wl.algorithmic_bytes(name)
+        assert k["ratio_to_algorithmic"] == 1.0
+        assert k["dispatches"] == 2
+    for name in bench.EXTRA:
+        k = rec["next_rows"][name]
+        assert k["bytes_per_launch"] == bench.EXTRA_BYTES[name]
         assert k["ratio_to_algorithmic"] == 1.0
         assert k["dispatches"] == 2
     # the figure is used only while the kernel sources hash the same
