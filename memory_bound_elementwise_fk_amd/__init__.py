@@ -117,28 +117,40 @@ def fk_status_string(status: int) -> str:
 
 
 # ------------------------------------------------------------ marshalling -
-def _torch():
-    import torch
+# These run on every call, so they keep to cheap tensor properties: a short
+# launch (attention at T = 128 takes 8.5 us on the device) is otherwise
+# bound by the host's argument checks.
+_torch_mod = None
+_dtype_codes = None
+_raw_stream = None
 
-    return torch
+
+def _torch():
+    global _torch_mod, _dtype_codes, _raw_stream
+    if _torch_mod is None:
+        import torch
+
+        _dtype_codes = {torch.float32: FK_F32, torch.bfloat16: FK_BF16, torch.float16: FK_F16}
+        # the current stream's handle for a device index, without building a
+        # torch.cuda.Stream object per call (that costs ~2 us)
+        _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        _torch_mod = torch
+    return _torch_mod
 
 
 def _dtype_code(t) -> int:
-    torch = _torch()
-    if t.dtype == torch.float32:
-        return FK_F32
-    if t.dtype == torch.bfloat16:
-        return FK_BF16
-    if t.dtype == torch.float16:
-        return FK_F16  # the library refuses it outside Linear and attention
-    raise TypeError(f"unsupported dtype {t.dtype} (float32, bfloat16, or float16 for Linear and attention)")
+    _torch()
+    code = _dtype_codes.get(t.dtype)
+    if code is None:  # FK_F16 is refused by the library outside Linear and attention
+        raise TypeError(f"unsupported dtype {t.dtype} (float32, bfloat16, or float16 for Linear and attention)")
+    return code
 
 
 def _device_tensor(t, name: str):
     torch = _torch()
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor, got device {t.device}")
 
 
@@ -146,14 +158,17 @@ def _on_device(t):
     """Context making t's GPU current for the call: a no-op when it already
     is (entering torch.cuda.device costs a few microseconds per call)."""
     torch = _torch()
-    if t.device.index is None or t.device.index == torch.cuda.current_device():
+    if t.get_device() == torch.cuda.current_device():
         return contextlib.nullcontext()
     return torch.cuda.device(t.device)
 
 
 def _stream_handle(t, stream) -> int | None:
     if stream is None:
-        return _torch().cuda.current_stream(t.device).cuda_stream
+        torch = _torch()
+        if _raw_stream is not None:
+            return _raw_stream(t.get_device())
+        return torch.cuda.current_stream(t.device).cuda_stream
     return getattr(stream, "cuda_stream", stream)
 
 
@@ -380,16 +395,19 @@ def fk_linear_gelu(x, w, bias, y, gelu: bool = True, stream=None, activation: st
 def fk_attention_fwd(q, k, v, o, causal: bool = True, stream=None) -> None:
     """o = softmax(q k^T / sqrt(d) + mask) v for 4-D [B, H, T, d] tensors (any strides,
     contiguous head dimension)."""
+    strides = []
     for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
         _device_tensor(t, name)
-        if t.dim() != 4 or tuple(t.shape) != tuple(q.shape):
+        if t.dim() != 4 or t.shape != q.shape:
             raise ValueError(f"fk_attention_fwd: {name} must be 4-D [B, H, T, d] like q")
-        if t.shape[3] > 1 and t.stride(3) != 1:
+        ts = t.stride()
+        if t.shape[3] > 1 and ts[3] != 1:
             raise ValueError(f"fk_attention_fwd: {name} needs a contiguous head dimension")
         if t.dtype != q.dtype:
             raise TypeError("fk_attention_fwd: q, k, v, o must share a dtype")
+        strides += ts[:3]
     B, H, T, d = q.shape
-    st = (ctypes.c_int64 * 12)(*[int(t.stride(i)) for t in (q, k, v, o) for i in range(3)])
+    st = (ctypes.c_int64 * 12)(*strides)
     with _on_device(q):
         _check(lib().fk_attention_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B,
                                       H, T, d, st, int(bool(causal)), _dtype_code(q),
