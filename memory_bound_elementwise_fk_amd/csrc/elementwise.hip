@@ -60,6 +60,46 @@ hipError_t launch_ew(const void* x, void* y, int64_t n, const Op& op, hipStream_
                          grid_for((n + tile - 1) / tile, kScalarT), kScalarT, s, x, y, n, op);
 }
 
+template <class IO, int K0, int K1, int K2>
+hipError_t launch_aaa(const void* x, void* y, int64_t n, const OpList& ops, hipStream_t s) {
+    return launch_ew<IO>(x, y, n, AffActAffOp<K0, K1, K2>{ops.scalar[0], ops.scalar[2]}, s);
+}
+
+// The fixed-kind kernel of an "add/mul, GELU/ReLU, add/mul" list.
+template <class IO>
+hipError_t launch_aaa_family(const void* x, void* y, int64_t n, const OpList& ops, hipStream_t s) {
+    const bool add0 = ops.kind[0] == kOpAdd, gelu = ops.kind[1] == kOpGelu,
+               add2 = ops.kind[2] == kOpAdd;
+    if (add0) {
+        if (gelu) return add2 ? launch_aaa<IO, kOpAdd, kOpGelu, kOpAdd>(x, y, n, ops, s)
+                              : launch_aaa<IO, kOpAdd, kOpGelu, kOpMul>(x, y, n, ops, s);
+        return add2 ? launch_aaa<IO, kOpAdd, kOpRelu, kOpAdd>(x, y, n, ops, s)
+                    : launch_aaa<IO, kOpAdd, kOpRelu, kOpMul>(x, y, n, ops, s);
+    }
+    if (gelu) return add2 ? launch_aaa<IO, kOpMul, kOpGelu, kOpAdd>(x, y, n, ops, s)
+                          : launch_aaa<IO, kOpMul, kOpGelu, kOpMul>(x, y, n, ops, s);
+    return add2 ? launch_aaa<IO, kOpMul, kOpRelu, kOpAdd>(x, y, n, ops, s)
+                : launch_aaa<IO, kOpMul, kOpRelu, kOpMul>(x, y, n, ops, s);
+}
+
+bool is_scalar_op(int32_t k) { return k == kOpAdd || k == kOpMul; }
+bool is_activation(int32_t k) { return k == kOpGelu || k == kOpRelu; }
+
+// One of the fixed-kind three-op chains.
+bool chain_is_aaa(const OpList& ops) {
+    return ops.n == 3 && is_scalar_op(ops.kind[0]) && is_activation(ops.kind[1]) &&
+           is_scalar_op(ops.kind[2]);
+}
+
+template <class IO>
+hipError_t launch_chain_t(const void* x, void* y, int64_t n, const OpList& ops, hipStream_t s) {
+    // the fixed-kind kernels serve aligned data; the scalar (unaligned)
+    // path keeps the general op loop
+    if (chain_is_aaa(ops) && aligned16(x) && aligned16(y))
+        return launch_aaa_family<IO>(x, y, n, ops, s);
+    return launch_ew<IO>(x, y, n, ChainOp{ops}, s);
+}
+
 }  // namespace
 
 hipError_t launch_gelu(const void* x, void* y, int64_t n, Dtype dt, hipStream_t s) {
@@ -69,8 +109,8 @@ hipError_t launch_gelu(const void* x, void* y, int64_t n, Dtype dt, hipStream_t 
 
 hipError_t launch_chain(const void* x, void* y, int64_t n, Dtype dt, const OpList& ops,
                         hipStream_t s) {
-    const ChainOp op{ops};
-    return dt == kF32 ? launch_ew<IoF32>(x, y, n, op, s) : launch_ew<IoBF16>(x, y, n, op, s);
+    return dt == kF32 ? launch_chain_t<IoF32>(x, y, n, ops, s)
+                      : launch_chain_t<IoBF16>(x, y, n, ops, s);
 }
 
 hipError_t launch_copy(const void* x, void* y, int64_t nbytes, hipStream_t s) {

@@ -56,6 +56,31 @@ struct ChainOp {
     }
 };
 
+// The three-op chains "scalar op, activation, scalar op" (K0 and K2 each
+// kOpAdd or kOpMul, K1 kOpGelu or kOpRelu; C3's 0.5 * GELU(x + 1) is one)
+// with the op kinds fixed at compile time: straight-line code, which the
+// compiler schedules across the three ops, instead of ChainOp's branch per op
+// (measured 2-3 % faster on a 32 MiB chain, where each wave's arithmetic
+// after its load returns adds to the kernel's latency). Same rounding as
+// ChainOp: each op rounds to fp32.
+template <int K0, int K1, int K2>
+struct AffActAffOp {
+    float s0, s2;
+    template <int N>
+    __device__ inline void operator()(float (&v)[N]) const {
+#pragma unroll
+        for (int j = 0; j < N; ++j) v[j] = K0 == kOpAdd ? v[j] + s0 : v[j] * s0;
+        if constexpr (K1 == kOpGelu) {
+            gelu_tanh_n(v);
+        } else {
+#pragma unroll
+            for (int j = 0; j < N; ++j) v[j] = relu1(v[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < N; ++j) v[j] = K2 == kOpAdd ? v[j] + s2 : v[j] * s2;
+    }
+};
+
 // Unpack U 16-byte words, apply the op to all their values at once, repack.
 template <class IO, int U, class Op>
 __device__ inline void ew_apply(u32x4 (&w)[U], const Op& op) {

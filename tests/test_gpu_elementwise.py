@@ -233,6 +233,41 @@ def test_ragged_tile_matches_full_tile_bitwise(dt, n, op):
     assert np.array_equal(bits[n - rest:], bits[:rest]), f"{op} {dt} n={n}: ragged tile differs"
 
 
+# "scalar op, activation, scalar op" lists run a kernel with the kinds fixed
+# at compile time when the data is 16-byte aligned; unaligned data runs the
+# general op loop. Both must give the same bits, and match the oracle.
+AAA = [(k0, k1, k2) for k0 in (fk.FK_OP_ADD_SCALAR, fk.FK_OP_MUL_SCALAR)
+       for k1 in (fk.FK_OP_GELU_TANH, fk.FK_OP_RELU)
+       for k2 in (fk.FK_OP_ADD_SCALAR, fk.FK_OP_MUL_SCALAR)]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("kinds", AAA, ids=["-".join(map(str, k)) for k in AAA])
+def test_fixed_kind_chains_match_the_op_loop_and_the_oracle(dt, kinds):
+    n = 3 * 4096 + 8 * 5 + 3   # full tiles, masked vectors, scalar tail
+    # a positive trailing add: GELU(v) >= -0.17, so GELU(v) + 1.25 never cancels
+    ops = [(kinds[0], 0.75), (kinds[1], 0.0), (kinds[2], 1.25)]
+    flat = random_input((n + 1,), dt, 4.0, seed=sum(kinds) + (dt == "bf16"))
+    if dt == "f32":
+        flat[1:7] = np.float32([0.0, -0.0, np.inf, -np.inf, np.nan, -30.0])
+    base = to_dev(flat)
+    aligned = base[:n].clone()               # 16-byte aligned: fixed-kind kernel
+    x = flat[:n]
+    full, y = guarded((n,), tdtype(dt))
+    fk.fk_elementwise_chain(aligned, y, ops)
+    got = to_host(y)
+    assert guards_intact(full, n)
+    check(dt, got, oracle.chain(x, ops), f"fixed-kind chain {kinds} {dt}")
+    # the same values through the general op loop (unaligned input)
+    yu = torch.empty(n + 1, dtype=tdtype(dt), device=DEV)[1:]
+    xu = torch.empty(n + 1, dtype=tdtype(dt), device=DEV)[1:]
+    xu.copy_(aligned)
+    fk.fk_elementwise_chain(xu, yu, ops)
+    gen = to_host(yu)
+    bits = np.uint32 if dt == "f32" else np.uint16
+    assert np.array_equal(got.view(bits), gen.view(bits)), "fixed-kind kernel differs from the op loop"
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("n", [1, 7, 4097, 50_001])
 def test_chain_long_op_lists(dt, n):
