@@ -6,11 +6,10 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * Pointers: x and y are DEVICE pointers owned by the caller. The library
- *   never synchronises and never copies device memory; the only memory it
- *   allocates is the small stream-ordered workspace of fk_softmax_rows on
- *   rows wider than on-chip capacity (fk_softmax_rows_ws takes it from the
- *   caller instead). Op lists (fk_op arrays) are HOST pointers, read before
- *   the call returns.
+ *   never allocates, frees, copies or synchronises device memory: the one
+ *   scratch buffer a kernel uses (the split softmax's partial statistics)
+ *   is the caller's, passed to fk_softmax_rows_ws. Op lists (fk_op arrays)
+ *   are HOST pointers, read before the call returns.
  * Stream: a hipStream_t passed as void*; NULL is the null stream. Work is
  *   enqueued on it and the call returns without waiting (launches are
  *   asynchronous, as the profiling notes on the pages stress: the host runs
@@ -107,18 +106,15 @@ int fk_elementwise_chain(const void* x, void* y, int64_t n, int dtype,
  * section 5.2: one block per row, max, exponentials and their sum,
  * normalise and write back). Entries past cols in a row (the stride
  * padding) are neither read nor written. fp32 accumulation.
- * Every path reads each element from HBM once and writes it once, except
- * the online fallback:
- *  - rows up to fk_softmax_onchip_max_cols(dtype) columns: one workgroup
- *    (or one wave) per row, the row held in registers;
- *  - wider rows, up to 64 slices of 8192 columns: the row is split over
- *    several workgroups that each hold one slice in registers and exchange
- *    partial (max, sum) pairs through a workspace, merged with the online
- *    softmax rule of "Lecture 6: GPU Kernels and Triton", section 7.2;
- *    fk_softmax_rows allocates that workspace itself (hipMallocAsync,
- *    zeroed by a kernel, hipFreeAsync, all on `stream`);
- *  - otherwise (or if that allocation fails): the online two-pass kernel
- *    (see fk_softmax_rows_online), which reads the row twice.
+ * Paths (fk_softmax_rows_path tells which one a call takes):
+ *  - FK_PATH_ONCHIP, rows up to fk_softmax_onchip_max_cols(dtype) columns:
+ *    one workgroup (or one wave) per row, the row held in registers; each
+ *    element is read from HBM once and written once;
+ *  - FK_PATH_ONLINE, wider rows: the online two-pass kernel of
+ *    fk_softmax_rows_online (one workgroup per row; the part of the row that
+ *    does not stay on chip is read twice).
+ * fk_softmax_rows_ws reads wide rows once instead (FK_PATH_SPLIT), with a
+ * caller workspace. Allocates nothing.
  * A row with NaN or +inf, or only -inf, comes out all NaN (the formula).
  * ldx, ldy: row strides in elements, >= cols.
  */
@@ -126,28 +122,60 @@ int fk_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols,
                     int64_t ldx, int64_t ldy, int dtype, void* stream);
 
 /*
- * fk_softmax_rows with a caller-owned workspace for the split path; the
- * library then allocates nothing. workspace: DEVICE memory of at least
- * fk_softmax_workspace_bytes(rows, cols, dtype) bytes, 8-byte aligned,
- * all zero before its first use; every completed call leaves it all zero
- * again, so it is zeroed once and reused. Calls that share a workspace must
- * not run concurrently (order them on one stream). When that size is 0 the
- * workspace is ignored and may be NULL. Errors: FK_ERR_INVALID_ARG for a
- * missing, misaligned or too small workspace or workspace_bytes < 0;
- * FK_ERR_OVERLAP if it overlaps x or y.
+ * fk_softmax_rows with a caller workspace for rows wider than on-chip
+ * capacity (FK_PATH_SPLIT): each row is cut into slices of 8192 columns
+ * (at most 64), one workgroup per slice holding it in registers, so every
+ * element is read from HBM once and written once. The slices of a row
+ * exchange partial (max, sum) pairs through the workspace and merge them
+ * with the online softmax rule of "Lecture 6: GPU Kernels and Triton",
+ * section 7.2.
+ * workspace: DEVICE memory of at least fk_softmax_workspace_bytes(rows,
+ *   cols, dtype) bytes, 8-byte aligned, with ANY contents: every slot word
+ *   carries a tag drawn afresh for each call, so zeros, a previous call's
+ *   partials or garbage are never read as this call's. Nothing needs
+ *   clearing before or after a call. Calls sharing a workspace should be
+ *   ordered (one stream): overlapping ones overwrite each other's slots,
+ *   which sends the affected workgroups to their bounded-wait fallback
+ *   (still correct, slower; see fk_set_split_wait_limit).
+ * The workspace is not used -- and may be NULL -- when that size is 0, and
+ * in place (y == x), where wide rows take FK_PATH_ONLINE: a split
+ * workgroup's fallback re-reads the whole row, which other slices may
+ * already have overwritten.
+ * Errors: FK_ERR_INVALID_ARG for a missing, misaligned or too small
+ * workspace (when it is used) or workspace_bytes < 0; FK_ERR_OVERLAP if it
+ * overlaps x or y.
  */
 int fk_softmax_rows_ws(const void* x, void* y, int64_t rows, int64_t cols,
                        int64_t ldx, int64_t ldy, int dtype, void* workspace,
                        int64_t workspace_bytes, void* stream);
 
 /*
- * Bytes of zeroed workspace the split path needs for rows x cols of dtype:
- * rows * slices * 8 + rows * 4 (rounded up to 8), with
- * slices = ceil(cols / 8192); 0 when the rows fit on chip or the split path
- * does not apply. FK_ERR_INVALID_ARG for negative sizes or an unknown
- * dtype. Pure host query.
+ * Bytes of workspace the split path needs for rows x cols of dtype:
+ * rows * slices * 16 (two 8-byte words per slice), slices = ceil(cols /
+ * 8192); 0 when the rows fit on chip or the split path does not apply
+ * (more than 64 slices). FK_ERR_INVALID_ARG for negative sizes or an
+ * unknown dtype. Pure host query.
  */
 int64_t fk_softmax_workspace_bytes(int64_t rows, int64_t cols, int dtype);
+
+/* Kernel paths of the row softmax. */
+typedef enum {
+    FK_PATH_NONE = 0,   /* empty work: nothing launched              */
+    FK_PATH_ONCHIP = 1, /* one row per workgroup, held in registers  */
+    FK_PATH_SPLIT = 2,  /* slices of a row over several workgroups   */
+    FK_PATH_ONLINE = 3  /* one workgroup streams the row twice       */
+} fk_softmax_path;
+
+/*
+ * The path (an fk_softmax_path) that fk_softmax_rows_ws takes for these
+ * arguments with a workspace of workspace_bytes bytes; workspace_bytes = 0
+ * gives the path of fk_softmax_rows. Arguments that call would reject
+ * return its negative fk_status. Pure host query: x and y are compared
+ * (y == x selects the in-place path), never dereferenced.
+ */
+int fk_softmax_rows_path(const void* x, const void* y, int64_t rows,
+                         int64_t cols, int64_t ldx, int64_t ldy, int dtype,
+                         int64_t workspace_bytes);
 
 /*
  * Bound on the polls (each followed by a short sleep) that a split-path
@@ -155,8 +183,9 @@ int64_t fk_softmax_workspace_bytes(int64_t rows, int64_t cols, int dtype);
  * workgroup computes the row's max and sum by streaming the whole row
  * itself, so the kernel ends and stays correct whatever the scheduling.
  * Default 2^20. Returns the previous bound, or FK_ERR_INVALID_ARG for
- * polls < 0. Process-wide; for tests and diagnostics (0 forces every
- * split workgroup onto the streamed statistics).
+ * polls < 0. Process-wide; for tests and diagnostics (0: every split
+ * workgroup polls once, so all but those that find every partial already
+ * published take the streamed statistics).
  */
 int64_t fk_set_split_wait_limit(int64_t polls);
 
@@ -166,7 +195,11 @@ int64_t fk_set_split_wait_limit(int64_t polls);
  * rescaling l by exp(m_old - m_new) whenever the max grows ("Lecture 6:
  * GPU Kernels and Triton", section 7.2 "Online Softmax", without the
  * attention accumulator); partial (m, l) pairs merge by the same rule;
- * pass 2 re-reads the row and writes exp(x - m) / l. Any cols >= 1.
+ * pass 2 writes exp(x - m) / l. One workgroup per row. For 16-byte aligned
+ * rows of < 2^31 bytes the first 131072 fp32 or 262144 bf16 columns (whole
+ * 8192-column chunks, 512 KiB) stay on chip -- in VGPRs and LDS -- between
+ * the passes, so only the rest of the row is read twice; other rows are
+ * read twice. Any cols >= 1.
  */
 int fk_softmax_rows_online(const void* x, void* y, int64_t rows, int64_t cols,
                            int64_t ldx, int64_t ldy, int dtype, void* stream);

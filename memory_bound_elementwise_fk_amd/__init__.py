@@ -29,6 +29,10 @@ FK_OP_ADD_SCALAR = 1
 FK_OP_MUL_SCALAR = 2
 FK_OP_GELU_TANH = 3
 FK_OP_RELU = 4
+FK_PATH_NONE = 0
+FK_PATH_ONCHIP = 1
+FK_PATH_SPLIT = 2
+FK_PATH_ONLINE = 3
 FK_ACT_NONE = 0
 FK_ACT_GELU_TANH = 1
 FK_ACT_RELU = 2
@@ -38,6 +42,7 @@ FK_MAX_OPS = 8
 __all__ = [
     "FusedOpsError", "lib", "fk_gelu_tanh", "fk_elementwise_chain", "fk_softmax_rows",
     "fk_softmax_rows_online", "fk_softmax_rows_ws", "fk_softmax_workspace_bytes",
+    "fk_softmax_rows_path",
     "fk_set_split_wait_limit", "fk_softmax_onchip_max_cols", "fk_layernorm_rows",
     "fk_layernorm_max_cols", "fk_copy", "fk_status_string", "layernorm_rows",
     "fk_gelu_tanh_backward", "fk_softmax_rows_backward", "fk_softmax_backward_max_cols",
@@ -82,6 +87,8 @@ def lib() -> ctypes.CDLL:
         fn.restype = i32
     L.fk_softmax_rows_ws.argtypes = [vp, vp, i64, i64, i64, i64, i32, vp, i64, vp]
     L.fk_softmax_rows_ws.restype = i32
+    L.fk_softmax_rows_path.argtypes = [vp, vp, i64, i64, i64, i64, i32, i64]
+    L.fk_softmax_rows_path.restype = i32
     L.fk_softmax_workspace_bytes.argtypes = [i64, i64, i32]
     L.fk_softmax_workspace_bytes.restype = i64
     L.fk_set_split_wait_limit.argtypes = [i64]
@@ -252,8 +259,9 @@ def fk_softmax_rows_online(x, y, stream=None) -> None:
 
 
 def fk_softmax_rows_ws(x, y, workspace, stream=None) -> None:
-    """As fk_softmax_rows with a caller-owned workspace (a zeroed device
-    tensor of at least fk_softmax_workspace_bytes bytes; None when that is 0)."""
+    """As fk_softmax_rows with a caller-owned workspace (a device tensor of
+    at least fk_softmax_workspace_bytes bytes, any contents; None when that
+    is 0)."""
     rows, cols, ldx, ldy, dt = _rows_pair(x, y, "fk_softmax_rows_ws")
     if workspace is None:
         wptr, wbytes = None, 0
@@ -273,8 +281,19 @@ def _dtype_arg(dtype) -> int:
     return {torch.float32: FK_F32, torch.bfloat16: FK_BF16, torch.float16: FK_F16}.get(dtype, -1)
 
 
+def fk_softmax_rows_path(x, y, workspace_bytes: int = 0) -> int:
+    """FK_PATH_* of fk_softmax_rows_ws(x, y, <workspace of workspace_bytes>)
+    (workspace_bytes = 0: the path of fk_softmax_rows). Host query only."""
+    rows, cols, ldx, ldy, dt = _rows_pair(x, y, "fk_softmax_rows_path")
+    v = lib().fk_softmax_rows_path(x.data_ptr(), y.data_ptr(), rows, cols, ldx, ldy, dt,
+                                   int(workspace_bytes))
+    if v < 0:
+        raise FusedOpsError(int(v), "fk_softmax_rows_path")
+    return int(v)
+
+
 def fk_softmax_workspace_bytes(rows: int, cols: int, dtype) -> int:
-    """Zeroed workspace bytes fk_softmax_rows_ws needs (0: none)."""
+    """Workspace bytes fk_softmax_rows_ws needs (0: none)."""
     v = lib().fk_softmax_workspace_bytes(int(rows), int(cols), _dtype_arg(dtype))
     if v < 0:
         raise FusedOpsError(int(v), "fk_softmax_workspace_bytes")

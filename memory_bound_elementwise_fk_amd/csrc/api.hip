@@ -11,6 +11,10 @@ static_assert(FK_MAX_OPS == fk::kMaxOps, "op list size mismatch");
 static_assert(int(FK_OP_ADD_SCALAR) == int(fk::kOpAdd) && int(FK_OP_MUL_SCALAR) == int(fk::kOpMul) &&
                   int(FK_OP_GELU_TANH) == int(fk::kOpGelu) && int(FK_OP_RELU) == int(fk::kOpRelu),
               "op kind mismatch");
+static_assert(int(FK_PATH_ONCHIP) == int(fk::kPathOnChip) &&
+                  int(FK_PATH_SPLIT) == int(fk::kPathSplit) &&
+                  int(FK_PATH_ONLINE) == int(fk::kPathOnline),
+              "softmax path mismatch");
 static_assert(int(FK_F32) == int(fk::kF32) && int(FK_BF16) == int(fk::kBF16) &&
                   int(FK_F16) == int(fk::kF16),
               "dtype mismatch");
@@ -81,26 +85,20 @@ int softmax_launch(const void* x, void* y, int64_t rows, int64_t cols, int64_t l
                                          online, ws, ws_bytes, static_cast<hipStream_t>(stream)));
 }
 
-// Rows wider than on-chip capacity take the split path with a workspace the
-// call allocates, zeroes and frees in stream order; if the allocation fails
-// the online two-pass path runs instead.
-int softmax_self_managed(const void* x, void* y, int64_t rows, int64_t cols, int64_t ldx,
-                         int64_t ldy, int dtype, void* stream) {
-    const hipStream_t s = static_cast<hipStream_t>(stream);
+// Validation of fk_softmax_rows_ws's workspace, for a call that passed
+// check_rows with work to do: FK_OK when the split path does not apply or
+// the workspace serves it.
+int check_workspace(const void* x, const void* y, int64_t rows, int64_t cols, int64_t ldx,
+                    int64_t ldy, int dtype, const void* workspace, int64_t workspace_bytes) {
     const int64_t need = fk::softmax_workspace_bytes(rows, cols, static_cast<fk::Dtype>(dtype));
-    if (need > 0) {
-        void* ws = nullptr;
-        if (hipMallocAsync(&ws, static_cast<size_t>(need), s) == hipSuccess) {
-            hipError_t e = fk::launch_zero_fill(ws, need, s);
-            if (e == hipSuccess)
-                e = fk::launch_softmax(x, y, rows, cols, ldx, ldy, static_cast<fk::Dtype>(dtype),
-                                       false, ws, need, s);
-            const hipError_t f = hipFreeAsync(ws, s);
-            return hip_status(e != hipSuccess ? e : f);
-        }
-        (void)hipGetLastError();  // clear the failed allocation; use the online path
-    }
-    return softmax_launch(x, y, rows, cols, ldx, ldy, dtype, false, nullptr, 0, stream);
+    if (need == 0 || x == y) return FK_OK;  // no split path: the workspace is not used
+    if (workspace == nullptr || workspace_bytes < need) return FK_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 7u) != 0) return FK_ERR_INVALID_ARG;
+    const int64_t es = esize(dtype);
+    if (ranges_overlap(workspace, need, x, ((rows - 1) * ldx + cols) * es) ||
+        ranges_overlap(workspace, need, y, ((rows - 1) * ldy + cols) * es))
+        return FK_ERR_OVERLAP;
+    return FK_OK;
 }
 
 }  // namespace
@@ -144,7 +142,7 @@ int fk_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols, int64_t 
     bool skip = false;
     const int st = check_rows(x, y, rows, cols, ldx, ldy, dtype, &skip);
     if (st != FK_OK || skip) return st;
-    return softmax_self_managed(x, y, rows, cols, ldx, ldy, dtype, stream);
+    return softmax_launch(x, y, rows, cols, ldx, ldy, dtype, false, nullptr, 0, stream);
 }
 
 int fk_softmax_rows_ws(const void* x, void* y, int64_t rows, int64_t cols, int64_t ldx,
@@ -155,17 +153,21 @@ int fk_softmax_rows_ws(const void* x, void* y, int64_t rows, int64_t cols, int64
     if (st != FK_OK) return st;
     if (workspace_bytes < 0) return FK_ERR_INVALID_ARG;
     if (skip) return FK_OK;
-    const int64_t need = fk::softmax_workspace_bytes(rows, cols, static_cast<fk::Dtype>(dtype));
-    if (need > 0) {
-        if (workspace == nullptr || workspace_bytes < need) return FK_ERR_INVALID_ARG;
-        if ((reinterpret_cast<uintptr_t>(workspace) & 7u) != 0) return FK_ERR_INVALID_ARG;
-        const int64_t es = esize(dtype);
-        if (ranges_overlap(workspace, need, x, ((rows - 1) * ldx + cols) * es) ||
-            ranges_overlap(workspace, need, y, ((rows - 1) * ldy + cols) * es))
-            return FK_ERR_OVERLAP;
-    }
-    return softmax_launch(x, y, rows, cols, ldx, ldy, dtype, false, need > 0 ? workspace : nullptr,
-                          need, stream);
+    st = check_workspace(x, y, rows, cols, ldx, ldy, dtype, workspace, workspace_bytes);
+    if (st != FK_OK) return st;
+    return softmax_launch(x, y, rows, cols, ldx, ldy, dtype, false, workspace, workspace_bytes,
+                          stream);
+}
+
+int fk_softmax_rows_path(const void* x, const void* y, int64_t rows, int64_t cols, int64_t ldx,
+                         int64_t ldy, int dtype, int64_t workspace_bytes) {
+    bool skip = false;
+    int st = check_rows(x, y, rows, cols, ldx, ldy, dtype, &skip);
+    if (st != FK_OK) return st;
+    if (workspace_bytes < 0) return FK_ERR_INVALID_ARG;
+    if (skip) return FK_PATH_NONE;
+    return fk::softmax_path(rows, cols, static_cast<fk::Dtype>(dtype), x == y, false,
+                            workspace_bytes);
 }
 
 int64_t fk_softmax_workspace_bytes(int64_t rows, int64_t cols, int dtype) {

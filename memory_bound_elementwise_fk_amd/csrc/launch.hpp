@@ -27,20 +27,22 @@ hipError_t launch_copy(const void* x, void* y, int64_t nbytes, hipStream_t s);
 
 // Softmax over rows. Path: rows up to softmax_onchip_max_cols(dt) columns
 // run the single-pass kernel; wider rows run the split kernel when `ws`
-// holds at least softmax_workspace_bytes() zeroed bytes, else the online
-// two-pass kernel. online == true forces the online kernel.
+// holds at least softmax_workspace_bytes() bytes (any contents) and y != x,
+// else the online two-pass kernel. online == true forces the online kernel.
+enum SoftmaxPath : int { kPathOnChip = 1, kPathSplit = 2, kPathOnline = 3 };
 hipError_t launch_softmax(const void* x, void* y, int64_t rows, int64_t cols, int64_t ldx,
                           int64_t ldy, Dtype dt, bool online, void* ws, int64_t ws_bytes,
                           hipStream_t s);
+// The path launch_softmax takes for these arguments (rows, cols >= 1).
+SoftmaxPath softmax_path(int64_t rows, int64_t cols, Dtype dt, bool in_place, bool online,
+                         int64_t ws_bytes);
 int64_t softmax_onchip_max_cols(Dtype dt);
-// Zeroed workspace the split path needs for this shape; 0 if it does not apply.
+// Workspace the split path needs for this shape; 0 if it does not apply.
 int64_t softmax_workspace_bytes(int64_t rows, int64_t cols, Dtype dt);
 // Bound on the polls of a split-kernel block waiting for its row's other
 // slices; past it the block computes the row statistics itself.
 int64_t split_wait_limit();
 int64_t set_split_wait_limit(int64_t polls);
-// Fill nbytes (a multiple of 8, 8-byte aligned) with zeros on stream s.
-hipError_t launch_zero_fill(void* p, int64_t nbytes, hipStream_t s);
 
 // Fused LayerNorm (+ optional tanh-GELU) over rows of at most
 // layernorm_max_cols(dt) columns; gamma / beta may be null.

@@ -1,6 +1,6 @@
 // softmax.hip -- launchers of the row softmax kernels in softmax_kernels.hpp:
-// the single-pass kernel for rows up to the on-chip capacity, the online
-// two-pass kernel above it.
+// the single-pass kernel for rows up to the on-chip capacity; above it the
+// split kernel when the caller brings a workspace, else the online kernel.
 #include <atomic>
 
 #include <utility>
@@ -88,18 +88,41 @@ hipError_t dispatch_reg(int shape, const void* x, void* y, int64_t rows, int64_t
                               std::make_index_sequence<kNumRegShapes>{});
 }
 
-// Online shape: 1024 lanes per row, 16 values per lane per chunk.
+// Online shape: 1024 lanes per row, 16 values per lane per chunk, for
+// unaligned rows (the plain online kernel, which streams the whole row
+// twice). Aligned rows run the staged kernel with 512 lanes (two waves per
+// SIMD, up to 256 VGPRs per lane): 8192-column chunks, the first RREG held
+// in VGPRs and the next RLDS in LDS -- 131072 fp32 or 262144 bf16 columns
+// (512 KiB) of the row on chip, one workgroup per CU.
 constexpr int kOnlineThreads = 1024;
 template <class IO>
 constexpr int kOnlineVpl = IO::kVec == 4 ? 4 : 2;
+constexpr int kStagedThreads = 512;
+template <class IO>
+constexpr int kStagedVpl = IO::kVec == 4 ? 4 : 2;     // one 16-byte vector = 4 fp32 / 8 bf16
+template <class IO>
+constexpr int kStagedReg = IO::kVec == 4 ? 12 : 24;   // 192 VGPRs of raw words
+template <class IO>
+constexpr int kStagedLds = IO::kVec == 4 ? 4 : 8;     // 128 KiB of LDS
+
+// The staged kernel addresses a row with 32-bit byte offsets.
+constexpr int64_t kStagedMaxRowBytes = int64_t(1) << 31;
 
 template <class IO>
 hipError_t launch_online(const void* x, void* y, int64_t rows, int64_t cols, int64_t ldx,
                          int64_t ldy, bool vec, hipStream_t s) {
+    if (vec && cols * IO::kBytes < kStagedMaxRowBytes) {
+        const void* fn = reinterpret_cast<const void*>(
+            &softmax_staged_kernel<IO, kStagedThreads, kStagedVpl<IO>, kStagedReg<IO>,
+                                   kStagedLds<IO>, kRowNT>);
+        return launch_kernel(fn, clamp_grid(rows, kStagedThreads), kStagedThreads, s, x, y, rows,
+                             cols, ldx, ldy);
+    }
     constexpr int VPL = kOnlineVpl<IO>;
-    const void* fn =
-        vec ? reinterpret_cast<const void*>(&softmax_online_kernel<IO, kOnlineThreads, VPL, true>)
-            : reinterpret_cast<const void*>(&softmax_online_kernel<IO, kOnlineThreads, VPL, false>);
+    const void* fn = vec ? reinterpret_cast<const void*>(
+                               &softmax_online_kernel<IO, kOnlineThreads, VPL, true>)
+                         : reinterpret_cast<const void*>(
+                               &softmax_online_kernel<IO, kOnlineThreads, VPL, false>);
     return launch_kernel(fn, clamp_grid(rows, kOnlineThreads), kOnlineThreads, s, x, y, rows, cols,
                          ldx, ldy);
 }
@@ -112,6 +135,15 @@ template <class IO>
 constexpr int64_t kSplitWidth = int64_t(kSplitThreads) * 32;
 
 std::atomic<int64_t> g_split_wait_limit{int64_t(1) << 20};
+// Tag of the next split launch (never 0, so a zeroed workspace holds no
+// valid slot); wraps after 2^32 launches.
+std::atomic<uint32_t> g_split_epoch{0};
+
+uint32_t next_split_epoch() {
+    uint32_t e = g_split_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+    while (e == 0) e = g_split_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+    return e;
+}
 
 template <class IO>
 int64_t split_parts(int64_t rows, int64_t cols) {
@@ -122,10 +154,8 @@ int64_t split_parts(int64_t rows, int64_t cols) {
     return parts;
 }
 
-int64_t split_ws_bytes(int64_t rows, int64_t parts) {
-    const int64_t depart = (rows * 4 + 7) / 8 * 8;
-    return rows * parts * 8 + depart;
-}
+// two tagged 64-bit words per slice of every row
+int64_t split_ws_bytes(int64_t rows, int64_t parts) { return rows * parts * 16; }
 
 template <class IO>
 hipError_t launch_split(const void* x, void* y, int64_t rows, int64_t cols, int64_t ldx,
@@ -135,16 +165,33 @@ hipError_t launch_split(const void* x, void* y, int64_t rows, int64_t cols, int6
         vec ? reinterpret_cast<const void*>(&softmax_split_kernel<IO, kSplitThreads, VPL, true, kRowNT>)
             : reinterpret_cast<const void*>(&softmax_split_kernel<IO, kSplitThreads, VPL, false>);
     auto* slots = static_cast<unsigned long long*>(ws);
-    auto* depart = reinterpret_cast<unsigned int*>(slots + rows * parts);
     const int p = static_cast<int>(parts);
+    const uint32_t epoch = next_split_epoch();
     const int64_t spin = g_split_wait_limit.load(std::memory_order_relaxed);
     return launch_kernel(fn, rows * parts, kSplitThreads, s, x, y, rows, cols, ldx, ldy, p, slots,
-                         depart, spin);
+                         epoch, spin);
 }
 
-__global__ __launch_bounds__(256) void zero_fill_kernel(unsigned long long* p, int64_t n) {
-    const int64_t stride = int64_t(gridDim.x) * 256;
-    for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += stride) p[i] = 0ull;
+// The one place that decides the path: the launch below and the host query
+// softmax_path both call it.
+template <class IO>
+SoftmaxPath choose_path(int64_t rows, int64_t cols, bool in_place, bool online, int64_t ws_bytes,
+                        int* shape, int64_t* parts) {
+    if (!online) {
+        for (int i = 0; i < kNumRegShapes; ++i)
+            if (cols <= reg_capacity<IO>(kRegShapes[i])) {
+                *shape = i;
+                return kPathOnChip;
+            }
+        const int64_t p = split_parts<IO>(rows, cols);
+        // in place, the split path's fallback could re-read values that
+        // another slice of the row has already overwritten
+        if (p > 0 && !in_place && ws_bytes >= split_ws_bytes(rows, p)) {
+            *parts = p;
+            return kPathSplit;
+        }
+    }
+    return kPathOnline;
 }
 
 template <class IO>
@@ -152,14 +199,12 @@ hipError_t launch_softmax_t(const void* x, void* y, int64_t rows, int64_t cols, 
                             int64_t ldy, bool online, void* ws, int64_t ws_bytes, hipStream_t s) {
     const bool vec = ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15u) == 0 &&
                      (ldx * IO::kBytes) % 16 == 0 && (ldy * IO::kBytes) % 16 == 0;
-    if (!online) {
-        for (int i = 0; i < kNumRegShapes; ++i)
-            if (cols <= reg_capacity<IO>(kRegShapes[i]))
-                return dispatch_reg<IO>(i, x, y, rows, cols, ldx, ldy, vec, s);
-        const int64_t parts = split_parts<IO>(rows, cols);
-        if (parts > 0 && ws != nullptr && ws_bytes >= split_ws_bytes(rows, parts))
-            return launch_split<IO>(x, y, rows, cols, ldx, ldy, parts, ws, vec, s);
-    }
+    int shape = 0;
+    int64_t parts = 0;
+    const SoftmaxPath path =
+        choose_path<IO>(rows, cols, x == y, online, ws == nullptr ? 0 : ws_bytes, &shape, &parts);
+    if (path == kPathOnChip) return dispatch_reg<IO>(shape, x, y, rows, cols, ldx, ldy, vec, s);
+    if (path == kPathSplit) return launch_split<IO>(x, y, rows, cols, ldx, ldy, parts, ws, vec, s);
     return launch_online<IO>(x, y, rows, cols, ldx, ldy, vec, s);
 }
 
@@ -175,16 +220,17 @@ int64_t softmax_workspace_bytes(int64_t rows, int64_t cols, Dtype dt) {
     return parts > 0 ? split_ws_bytes(rows, parts) : 0;
 }
 
+SoftmaxPath softmax_path(int64_t rows, int64_t cols, Dtype dt, bool in_place, bool online,
+                         int64_t ws_bytes) {
+    int shape = 0;
+    int64_t parts = 0;
+    return dt == kF32 ? choose_path<IoF32>(rows, cols, in_place, online, ws_bytes, &shape, &parts)
+                      : choose_path<IoBF16>(rows, cols, in_place, online, ws_bytes, &shape, &parts);
+}
+
 int64_t split_wait_limit() { return g_split_wait_limit.load(); }
 
 int64_t set_split_wait_limit(int64_t polls) { return g_split_wait_limit.exchange(polls); }
-
-hipError_t launch_zero_fill(void* p, int64_t nbytes, hipStream_t s) {
-    const int64_t n = nbytes / 8;
-    const int64_t grid = n / 256 + 1 < 4096 ? n / 256 + 1 : 4096;
-    return launch_kernel(reinterpret_cast<const void*>(&zero_fill_kernel), grid, 256, s,
-                         static_cast<unsigned long long*>(p), n);
-}
 
 hipError_t launch_softmax(const void* x, void* y, int64_t rows, int64_t cols, int64_t ldx,
                           int64_t ldy, Dtype dt, bool online, void* ws, int64_t ws_bytes,

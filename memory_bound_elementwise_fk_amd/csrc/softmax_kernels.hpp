@@ -384,6 +384,276 @@ __global__ __launch_bounds__(THREADS) void softmax_online_kernel(
     }
 }
 
+// ---------------------------------------------------------- staged kernel -
+// The online two-pass kernel for 16-byte-aligned rows, keeping as much of the
+// row on chip as a 1024-lane workgroup can hold, so that only the rest is
+// read from HBM twice. The row is cut into chunks of THREADS * VPL 16-byte
+// vectors (one vector per lane per k < VPL, the layout of load_span); chunk
+// c < RREG stays in the lanes' VGPRs as raw 16-byte words, chunk
+// RREG <= c < RREG + RLDS in LDS, and the chunks after those are streamed.
+// Pass 1 updates a per-lane running max m and sum l chunk by chunk: when the
+// max grows, l is rescaled by 2^((m_old - m_new) log2e) ("Lecture 6: GPU
+// Kernels and Triton", section 7.2 "Online Softmax", without the attention
+// accumulator); the lanes' states then merge by the same rule (wave by DPP,
+// waves through LDS, a fixed order). Pass 2 normalises: the streamed chunks
+// are read again (last first: the most recently read bytes are the likeliest
+// to be in L2 or the Infinity Cache), the resident ones come from VGPRs and
+// LDS. Each resident element is read from HBM once and written once.
+//
+// With the launcher's shapes (16384-column chunks; fp32: RREG 5, RLDS 2,
+// bf16: RREG 8, RLDS 4) 114688 fp32 columns (448 KiB) or 196608 bf16
+// columns (384 KiB) stay on chip: a 1024 x 131072 fp32 row re-reads one
+// chunk in eight.
+template <class IO, int VPL, int LANES, bool NT>
+__device__ inline void load_raw_span(const char* xr, int64_t cols, int64_t c0, int lane,
+                                     u32x4 (&w)[VPL]) {
+    constexpr int V = IO::kVec;
+    constexpr int64_t kSpan = int64_t(VPL) * LANES * V;
+    if (cols - c0 >= kSpan) {
+#pragma unroll
+        for (int k = 0; k < VPL; ++k)
+            w[k] = ld16<NT>(reinterpret_cast<const u32x4*>(
+                xr + (c0 + (int64_t(k) * LANES + lane) * V) * IO::kBytes));
+        return;
+    }
+    // the row's last, partial chunk: whole vectors where they fit, single
+    // elements for the one straddling the row end, -inf past it (a bf16 or
+    // fp32 value widened and rounded back is itself, -inf included)
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+        const int64_t c = c0 + (int64_t(k) * LANES + lane) * V;
+        if (c + V <= cols) {
+            w[k] = ld16<NT>(reinterpret_cast<const u32x4*>(xr + c * IO::kBytes));
+        } else {
+            float v[V];
+#pragma unroll
+            for (int e = 0; e < V; ++e) v[e] = (c + e < cols) ? IO::load1(xr, c + e) : kNegInf;
+            w[k] = IO::pack(v);
+        }
+    }
+}
+
+// Per-lane online update of (m, l) with the values of one chunk.
+template <class IO, int VPL>
+__device__ inline void ml_update_raw(const u32x4 (&w)[VPL], float& m, float& l) {
+    constexpr int E = VPL * IO::kVec;
+    float v[E];
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) IO::unpack(w[k], &v[k * IO::kVec]);
+    float cm = kNegInf;
+#pragma unroll
+    for (int i = 0; i < E; ++i) cm = fmaxf(cm, v[i]);
+    const float mn = fmaxf(m, cm);
+    if (mn != kNegInf) {  // while every value seen is -inf, l stays 0
+        if (mn != m) l *= exp2_raw((m - mn) * kLog2e);
+        m = mn;
+#pragma unroll
+        for (int i = 0; i < E; ++i) l += exp2_raw((v[i] - m) * kLog2e);
+    }
+}
+
+// y for one chunk from its raw words: e' / (l 2^8), stored (masked past cols).
+template <class IO, int VPL, int LANES, bool NT>
+__device__ inline void normalise_store_raw(char* yr, int64_t cols, int64_t c0, int lane,
+                                           const u32x4 (&w)[VPL], float M, float r) {
+    constexpr int E = VPL * IO::kVec;
+    float v[E];
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) IO::unpack(w[k], &v[k * IO::kVec]);
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = softmax_numerator(v[i], M) * r;
+    store_span<IO, VPL, LANES, true, NT>(yr, cols, c0, lane, v);
+}
+
+// Resident chunks are loaded with buffer instructions: the row is one buffer
+// resource (scalar registers), every load of a lane shares one VGPR offset
+// (tid * 16) and adds a scalar offset per chunk and vector. Global loads
+// would need a 64-bit VGPR address each (the strides between a lane's
+// vectors exceed their immediate offsets), which the compiler computes ahead
+// and keeps live: that spilled. Rows of < 2^31 bytes only (32-bit offsets).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+// Word 3 of a raw buffer descriptor on this architecture family: data
+// format 32 bits (a zero format would make every access return 0).
+constexpr int kBufferWord3 = 0x00020000;
+
+__device__ inline rsrc_t row_buffer(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                             kBufferWord3);
+}
+
+// The VPL vectors of a lane in chunk c (a whole chunk: no masks). voff is
+// the lane's byte offset (tid * 16), chunk_bytes the chunk size in bytes.
+template <int VPL, int LANES, bool NT>
+__device__ inline void load_chunk_buf(rsrc_t rx, uint32_t voff, uint32_t c0_bytes,
+                                      u32x4 (&w)[VPL]) {
+#pragma unroll
+    for (int k = 0; k < VPL; ++k)
+        w[k] = __builtin_amdgcn_raw_buffer_load_b128(rx, voff, c0_bytes + k * LANES * 16, NT ? 2 : 0);
+}
+
+// The same chunk straight into LDS (buffer_load_dwordx4 ... lds, no VGPRs):
+// for vector k, wave w's 64 lanes write 16 bytes each, in lane order, at
+// &dst[k][w * 64], so lane tid's vector lands at dst[k][tid].
+template <int VPL, int LANES, bool NT>
+__device__ inline void load_chunk_lds(rsrc_t rx, uint32_t voff, uint32_t c0_bytes, int tid,
+                                      u32x4 (*dst)[LANES]) {
+    const int wave_base = (tid / kWave) * kWave;
+#pragma unroll
+    for (int k = 0; k < VPL; ++k)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rx, (__attribute__((address_space(3))) void*)(&dst[k][wave_base]), 16, voff,
+            c0_bytes + k * LANES * 16, 0, NT ? 2 : 0);
+}
+
+// y for one whole chunk, stored with global instructions from the row base
+// plus a 32-bit lane offset. (Buffer stores were tried here: in 512-lane
+// workgroups storing eight or more chunks per lane, lanes 12-15 of every
+// 16-lane group in waves 4-7 stored values that the next instruction had
+// already written into the store's data registers; global stores are
+// exact in the same kernel.)
+template <class IO, int VPL, int LANES, bool NT>
+__device__ inline void normalise_store_global(char* yr, uint32_t voff, uint32_t c0_bytes,
+                                              const u32x4 (&w)[VPL], float M, float r) {
+    constexpr int V = IO::kVec;
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+        float v[V];
+        IO::unpack(w[k], v);
+#pragma unroll
+        for (int e = 0; e < V; ++e) v[e] = softmax_numerator(v[e], M) * r;
+        const uint32_t off = c0_bytes + k * LANES * 16 + voff;
+        st16<NT>(reinterpret_cast<u32x4*>(yr + off), IO::pack(v));
+    }
+}
+
+// The lane index as an opaque value: everything computed from it after this
+// point stays after it. The masked chunk path derives per-lane columns and
+// 64-bit compares from the lane alone; left visible, the compiler hoists them
+// out of the row loop and keeps them live beside the resident chunks, which
+// then spill.
+__device__ inline int opaque_lane(int tid) {
+    asm volatile("" : "+v"(tid));
+    return tid;
+}
+
+template <class IO, int THREADS, int VPL, int RREG, int RLDS, bool NT>
+__global__ __launch_bounds__(THREADS) void softmax_staged_kernel(
+    const void* x, void* y, int64_t rows, int64_t cols, int64_t ldx, int64_t ldy) {
+    constexpr int64_t kChunk = int64_t(THREADS) * VPL * IO::kVec;
+    constexpr int kWaves = THREADS / kWave;
+    // LDS chunks as raw words, [chunk][vector k][lane]: a lane's 16 bytes of
+    // one k are contiguous with its neighbours' (conflict-free 128-bit access)
+    __shared__ u32x4 stage[RLDS > 0 ? RLDS : 1][VPL][THREADS];
+    __shared__ float red_m[kWaves];
+    __shared__ float red_l[kWaves];
+
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int wave = tid / kWave;
+    const int64_t nchunks = (cols + kChunk - 1) / kChunk;
+    const int64_t nfull = cols / kChunk;
+    // chunks from here on are streamed (read in both passes)
+    const int64_t first_streamed = nfull < RREG + RLDS ? nfull : RREG + RLDS;
+    const bool streams = first_streamed < nchunks;
+
+    constexpr uint32_t kChunkBytes = uint32_t(kChunk) * IO::kBytes;
+    const uint32_t voff = uint32_t(tid) * 16;
+    const uint32_t row_bytes = uint32_t(cols) * IO::kBytes;
+
+    for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+        const char* xr = row_ptr<IO>(x, row, ldx);
+        char* yr = row_ptr<IO>(y, row, ldy);
+        const rsrc_t rx = row_buffer(xr, row_bytes);
+
+        // pass 1: every load in flight first
+        u32x4 res[RREG][VPL];
+#pragma unroll
+        for (int c = 0; c < RREG; ++c)
+            if (c < nfull) load_chunk_buf<VPL, THREADS, NT>(rx, voff, c * kChunkBytes, res[c]);
+#pragma unroll
+        for (int c = RREG; c < RREG + RLDS; ++c)
+            if (c < nfull)
+                load_chunk_lds<VPL, THREADS, NT>(rx, voff, c * kChunkBytes, tid, stage[c - RREG]);
+        u32x4 t[VPL];
+        if (streams) load_raw_span<IO, VPL, THREADS, NT>(xr, cols, first_streamed * kChunk, opaque_lane(tid), t);
+
+        float m = kNegInf, l = 0.0f;
+#pragma unroll
+        for (int c = 0; c < RREG; ++c)
+            if (c < nfull) ml_update_raw<IO, VPL>(res[c], m, l);
+        // the LDS chunks: each lane reads back what its own loads wrote, once
+        // they have completed
+        __builtin_amdgcn_s_waitcnt(0);
+        // (one LDS chunk at a time: the scheduler would otherwise hoist
+        // every chunk's reads together, and the registers they need spill)
+#pragma unroll
+        for (int c = RREG; c < RREG + RLDS; ++c) {
+            if (c < nfull) {
+                u32x4 w[VPL];
+#pragma unroll
+                for (int k = 0; k < VPL; ++k) w[k] = stage[c - RREG][k][tid];
+                ml_update_raw<IO, VPL>(w, m, l);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (streams) ml_update_raw<IO, VPL>(t, m, l);
+        for (int64_t c = first_streamed + 1; c < nchunks; ++c) {
+            load_raw_span<IO, VPL, THREADS, NT>(xr, cols, c * kChunk, opaque_lane(tid), t);
+            ml_update_raw<IO, VPL>(t, m, l);
+        }
+
+        // merge the lanes' states: the wave (DPP), then the waves (LDS)
+        wave_ml(m, l);
+        if (lane == 0) {
+            red_m[wave] = m;
+            red_l[wave] = l;
+        }
+        __syncthreads();
+        float M = red_m[0], L = red_l[0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) ml_merge(M, L, red_m[w], red_l[w]);
+
+        // pass 2: e' carries the factor 2^8. bf16 resident words pass
+        // through an empty asm statement first, so the compiler unpacks them
+        // again here rather than keeping pass 1's unpacked values alive
+        // (twice the registers); fp32 words need no unpacking.
+        if constexpr (IO::kBytes == 2) {
+#pragma unroll
+            for (int c = 0; c < RREG; ++c)
+#pragma unroll
+                for (int k = 0; k < VPL; ++k) asm volatile("" : "+v"(res[c][k]));
+        }
+        const float r = 1.0f / (L * kSoftmaxScale);
+        if (streams)
+            load_raw_span<IO, VPL, THREADS, NT>(xr, cols, (nchunks - 1) * kChunk, opaque_lane(tid), t);
+#pragma unroll
+        for (int c = 0; c < RREG; ++c)
+            if (c < nfull)
+                normalise_store_global<IO, VPL, THREADS, NT>(yr, voff, c * kChunkBytes, res[c], M, r);
+#pragma unroll
+        for (int c = RREG; c < RREG + RLDS; ++c) {
+            if (c < nfull) {
+                u32x4 w[VPL];
+#pragma unroll
+                for (int k = 0; k < VPL; ++k) w[k] = stage[c - RREG][k][tid];
+                normalise_store_global<IO, VPL, THREADS, NT>(yr, voff, c * kChunkBytes, w, M, r);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (streams) {
+            normalise_store_raw<IO, VPL, THREADS, NT>(yr, cols, (nchunks - 1) * kChunk, opaque_lane(tid), t,
+                                                      M, r);
+            for (int64_t c = nchunks - 2; c >= first_streamed; --c) {
+                load_raw_span<IO, VPL, THREADS, NT>(xr, cols, c * kChunk, opaque_lane(tid), t);
+                normalise_store_raw<IO, VPL, THREADS, NT>(yr, cols, c * kChunk, opaque_lane(tid), t,
+                                                          M, r);
+            }
+        }
+        // the next row rewrites red_m / red_l and the LDS chunks
+        __syncthreads();
+    }
+}
+
 // ------------------------------------------------------------ split kernel -
 // Rows wider than one workgroup's registers, without re-reading HBM: the row
 // is cut into `parts` slices of THREADS*E columns, one workgroup per slice
@@ -396,12 +666,14 @@ __global__ __launch_bounds__(THREADS) void softmax_online_kernel(
 // of the row merges the same values in the same order, so all of them
 // normalise with bit-identical (M, L).
 //
-// Exchange: slot[row * parts + p] is one 64-bit word holding (m_p, l_p),
-// written and polled with relaxed device-scope atomics. Zero marks an empty
-// slot; no real partial is all-zero bits (a finite m_p implies l_p >= 1).
-// depart[row] counts the slices that are done with the slots; the last one
-// clears the row's slots and its counter, so the workspace is all zero again
-// when the kernel ends (it must be all zero before the first call).
+// Exchange: slot p of a row is two 64-bit words, (epoch << 32 | bits of
+// m_p) and (epoch << 32 | bits of l_p), written and polled with relaxed
+// device-scope atomics. `epoch` is a non-zero tag the host draws afresh for
+// every launch; a word counts only when it carries this launch's tag, so
+// whatever the workspace held before -- zeros, another call's partials,
+// garbage -- is never taken for a partial of this call (a stale word would
+// have to match the 32-bit tag in both words). The workspace therefore
+// needs no clearing before or after a call.
 //
 // The wait for the other slices is bounded by spin_limit polls. Slices of a
 // row are consecutive blocks, and blocks are dispatched in order, so the
@@ -409,14 +681,16 @@ __global__ __launch_bounds__(THREADS) void softmax_online_kernel(
 // the workgroup computes (M, L) by streaming the whole row itself (online
 // recurrence) and still normalises its own slice: correct and terminating
 // whatever the scheduling, at the cost of that row's bits possibly
-// differing in the last place between slices.
+// differing in the last place between slices. The streamed statistics
+// re-read x after other slices of the row may have written y, so the host
+// never sends an in-place call (y == x) down this path.
 constexpr int kSplitMaxParts = kWave;  // one lane polls one slot
 
-__device__ inline unsigned long long pack_ml(float m, float l) {
-    return (static_cast<unsigned long long>(__float_as_uint(l)) << 32) | __float_as_uint(m);
+__device__ inline unsigned long long tag_word(uint32_t epoch, float v) {
+    return (static_cast<unsigned long long>(epoch) << 32) | __float_as_uint(v);
 }
-__device__ inline float unpack_m(unsigned long long w) { return __uint_as_float(uint32_t(w)); }
-__device__ inline float unpack_l(unsigned long long w) { return __uint_as_float(uint32_t(w >> 32)); }
+__device__ inline uint32_t word_tag(unsigned long long w) { return uint32_t(w >> 32); }
+__device__ inline float word_value(unsigned long long w) { return __uint_as_float(uint32_t(w)); }
 
 // Block-wide max and sum over all THREADS lanes, fixed order, same bits in
 // every lane. `red` holds THREADS / 64 floats.
@@ -488,7 +762,7 @@ __device__ inline void row_stats_streamed(const char* xr, int64_t cols, float* r
 template <class IO, int THREADS, int VPL, bool VEC, bool NT = false>
 __global__ __launch_bounds__(THREADS) void softmax_split_kernel(
     const void* x, void* y, int64_t rows, int64_t cols, int64_t ldx, int64_t ldy, int parts,
-    unsigned long long* slots, unsigned int* depart, int64_t spin_limit) {
+    unsigned long long* slots, uint32_t epoch, int64_t spin_limit) {
     constexpr int E = VPL * IO::kVec;
     constexpr int64_t kW = int64_t(THREADS) * E;
     constexpr int kWaves = THREADS / kWave;
@@ -522,27 +796,36 @@ __global__ __launch_bounds__(THREADS) void softmax_split_kernel(
         }
         l = block_sum<THREADS>(l, red_l);
 
-        unsigned long long* row_slots = slots + row * parts;
-        if (tid == 0)
-            __hip_atomic_store(row_slots + p, pack_ml(m, l), __ATOMIC_RELAXED,
+        unsigned long long* row_slots = slots + 2 * (row * parts);
+        if (tid == 0) {
+            __hip_atomic_store(row_slots + 2 * p, tag_word(epoch, m), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(row_slots + 2 * p + 1, tag_word(epoch, l), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
 
         // wave 0 gathers every slice's partial and merges them in slice order
         if (tid < kWave) {
-            unsigned long long w = 0;
+            float pm = kNegInf, pl = 0.0f;  // lanes past the slices hold the empty state
             bool gathered = false;
             for (int64_t it = 0;; ++it) {
-                w = lane < parts ? __hip_atomic_load(row_slots + lane, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT)
-                                 : pack_ml(kNegInf, 0.0f);
-                if (__builtin_amdgcn_ballot_w64(w == 0) == 0) {
+                bool have = true;
+                if (lane < parts) {
+                    const unsigned long long wm = __hip_atomic_load(
+                        row_slots + 2 * lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    const unsigned long long wl = __hip_atomic_load(
+                        row_slots + 2 * lane + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    have = word_tag(wm) == epoch && word_tag(wl) == epoch;
+                    pm = word_value(wm);
+                    pl = word_value(wl);
+                }
+                if (__builtin_amdgcn_ballot_w64(!have) == 0) {
                     gathered = true;
                     break;
                 }
                 if (it >= spin_limit) break;
                 __builtin_amdgcn_s_sleep(2);
             }
-            float pm = unpack_m(w), pl = unpack_l(w);
             wave_ml(pm, pl);
             if (tid == 0) {
                 merged[0] = pm;
@@ -561,18 +844,6 @@ __global__ __launch_bounds__(THREADS) void softmax_split_kernel(
 #pragma unroll
         for (int i = 0; i < E; ++i) v[i] = softmax_numerator(v[i], M) * r;
         store_span<IO, VPL, THREADS, VEC, NT>(row_ptr<IO>(y, row, ldy), cols, c0, tid, v);
-
-        // the last slice done with the row's slots clears them
-        if (tid == 0) {
-            const unsigned int done =
-                __hip_atomic_fetch_add(depart + row, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (done == static_cast<unsigned int>(parts - 1)) {
-                for (int q = 0; q < parts; ++q)
-                    __hip_atomic_store(row_slots + q, 0ull, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(depart + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
     }
 }
 

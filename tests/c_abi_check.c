@@ -49,7 +49,13 @@ int main(void) {
     CHECK(fk_layernorm_max_cols(FK_F32) == 32768);
     CHECK(fk_softmax_backward_max_cols(FK_BF16) == 32768);
     CHECK(fk_softmax_workspace_bytes(16, 1000, FK_F32) == 0);      /* on chip: none */
-    CHECK(fk_softmax_workspace_bytes(1024, 131072, FK_F32) > 0);   /* split rows */
+    CHECK(fk_softmax_workspace_bytes(1024, 131072, FK_F32) == 1024 * 16 * 16); /* split rows */
+    CHECK(fk_softmax_rows_path(a, b, 1024, 131072, 131072, 131072, FK_F32, 0) == FK_PATH_ONLINE);
+    CHECK(fk_softmax_rows_path(a, b, 1024, 131072, 131072, 131072, FK_F32, 1 << 18) ==
+          FK_PATH_SPLIT);
+    CHECK(fk_softmax_rows_path(a, a, 1024, 131072, 131072, 131072, FK_F32, 1 << 18) ==
+          FK_PATH_ONLINE);
+    CHECK(fk_softmax_rows_path(a, b, 16, 1000, 1000, 1000, FK_F32, 0) == FK_PATH_ONCHIP);
 
     /* empty work: FK_OK, nothing launched, NULL pointers allowed */
     CHECK(fk_gelu_tanh(NULL, NULL, 0, FK_F32, NULL) == FK_OK);

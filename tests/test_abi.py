@@ -43,7 +43,8 @@ def test_header_declares_the_entry_points():
                  "fk_set_split_wait_limit", "fk_softmax_onchip_max_cols", "fk_copy",
                  "fk_status_string", "fk_layernorm_rows", "fk_layernorm_max_cols",
                  "fk_gelu_tanh_backward", "fk_softmax_rows_backward",
-                 "fk_softmax_backward_max_cols", "fk_linear_gelu", "fk_attention_fwd"):
+                 "fk_softmax_backward_max_cols", "fk_linear_gelu", "fk_attention_fwd",
+                 "fk_softmax_rows_path"):
         assert want in names
 
 
@@ -130,11 +131,11 @@ def test_softmax_workspace_query(L):
     assert q(4096, 32768, fk.FK_F32) == 0
     assert q(10, 65536, fk.FK_BF16) == 0
     assert q(0, 10**6, fk.FK_F32) == 0 and q(10, 0, fk.FK_F32) == 0
-    # rows * slices * 8 + rows * 4 rounded up to 8, slices = ceil(cols / 8192)
-    assert q(1024, 131072, fk.FK_F32) == 1024 * 16 * 8 + 4096
-    assert q(3, 32769, fk.FK_F32) == 3 * 5 * 8 + 16
-    assert q(7, 65537, fk.FK_BF16) == 7 * 9 * 8 + 32
-    assert q(1, 64 * 8192, fk.FK_F32) == 64 * 8 + 8
+    # rows * slices * 16 (two tagged 8-byte words per slice), slices = ceil(cols / 8192)
+    assert q(1024, 131072, fk.FK_F32) == 1024 * 16 * 16
+    assert q(3, 32769, fk.FK_F32) == 3 * 5 * 16
+    assert q(7, 65537, fk.FK_BF16) == 7 * 9 * 16
+    assert q(1, 64 * 8192, fk.FK_F32) == 64 * 16
     assert q(1, 64 * 8192 + 1, fk.FK_F32) == 0      # beyond 64 slices: online path
     assert q(-1, 10, fk.FK_F32) == fk.FK_ERR_INVALID_ARG
     assert q(1, 10, 9) == fk.FK_ERR_INVALID_ARG
@@ -154,6 +155,43 @@ def test_softmax_ws_validation(L):
     assert s(A, B, rows, cols, cols, cols, 0, B, need, None) == fk.FK_ERR_OVERLAP
     assert s(A, B, 0, cols, cols, cols, 0, None, 0, None) == fk.FK_OK     # empty
     assert s(A, B, rows, cols, cols - 1, cols, 0, W, need, None) == fk.FK_ERR_INVALID_ARG
+
+
+def test_softmax_path_query(L):
+    p = L.fk_softmax_rows_path
+    A, B = 0x7F0000000000, 0x7F8000000000   # 512 GiB apart: the shapes below never overlap
+    F32, BF16 = fk.FK_F32, fk.FK_BF16
+    need = L.fk_softmax_workspace_bytes(1024, 131072, F32)
+    # rows on chip, whatever the workspace
+    assert p(A, B, 4096, 1000, 1000, 1000, F32, 0) == fk.FK_PATH_ONCHIP
+    assert p(A, B, 32768, 4096, 4096, 4096, BF16, 0) == fk.FK_PATH_ONCHIP
+    assert p(A, B, 3, 32768, 32768, 32768, F32, 0) == fk.FK_PATH_ONCHIP
+    assert p(A, B, 3, 65536, 65536, 65536, BF16, 1 << 20) == fk.FK_PATH_ONCHIP
+    # wide rows: split with a large enough workspace, online without one
+    assert p(A, B, 1024, 131072, 131072, 131072, F32, need) == fk.FK_PATH_SPLIT
+    assert p(A, B, 1024, 131072, 131072, 131072, F32, need - 1) == fk.FK_PATH_ONLINE
+    assert p(A, B, 1024, 131072, 131072, 131072, F32, 0) == fk.FK_PATH_ONLINE
+    assert p(A, B, 3, 32769, 32769, 32769, F32, 3 * 5 * 16) == fk.FK_PATH_SPLIT
+    # in place: never split (its fallback would re-read overwritten values)
+    assert p(A, A, 1024, 131072, 131072, 131072, F32, need) == fk.FK_PATH_ONLINE
+    # more than 64 slices: online
+    wide = 64 * 8192 + 1
+    assert p(A, B, 2, wide, wide, wide, F32, 1 << 30) == fk.FK_PATH_ONLINE
+    # empty work, and arguments the call would refuse
+    assert p(A, B, 0, 10, 10, 10, F32, 0) == fk.FK_PATH_NONE
+    assert p(None, None, 5, 0, 0, 0, F32, 0) == fk.FK_PATH_NONE
+    assert p(A, B, 4, 10, 9, 10, F32, 0) == fk.FK_ERR_INVALID_ARG
+    assert p(A, B, 4, 10, 10, 10, F32, -1) == fk.FK_ERR_INVALID_ARG
+    assert p(A, A + 40, 4, 10, 20, 20, F32, 0) == fk.FK_ERR_OVERLAP
+    assert p(A, B, 4, 10, 10, 10, 9, 0) == fk.FK_ERR_INVALID_ARG
+    assert p(A, B, 4, 10, 10, 10, fk.FK_F16, 0) == fk.FK_ERR_UNSUPPORTED
+
+
+def test_softmax_ws_in_place_ignores_the_workspace(L):
+    # wide rows in place take the online path, so the workspace is not
+    # validated (it may be NULL); refusals of the row arguments still apply
+    s = L.fk_softmax_rows_ws
+    assert s(A, A, 4, 40000, 40000, 40001, 0, None, 0, None) == fk.FK_ERR_OVERLAP
 
 
 def test_split_wait_limit(L):

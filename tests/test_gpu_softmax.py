@@ -51,14 +51,15 @@ def test_c4_softmax_bf16_full_size():
     assert np.all(got[x == wl.BF16_MINUS_1E4] == 0)        # masked entries are exactly 0
 
 
-def test_c5a_softmax_fp32_full_size_self_managed():
-    # wider than on-chip capacity: fk_softmax_rows takes the split path with
-    # a workspace it allocates itself
+def test_c5a_softmax_fp32_full_size_no_workspace():
+    # wider than on-chip capacity: without a workspace fk_softmax_rows takes
+    # the online path (it allocates nothing)
     x = wl.make_input("C5a")
     assert x.shape[1] > fk.fk_softmax_onchip_max_cols(torch.float32)
     assert fk.fk_softmax_workspace_bytes(*x.shape, torch.float32) > 0
     xt = to_dev(x)
     y = torch.empty_like(xt)
+    assert fk.fk_softmax_rows_path(xt, y) == fk.FK_PATH_ONLINE
     fk.fk_softmax_rows(xt, y)
     got = to_host(y)
     del xt, y
