@@ -44,7 +44,7 @@ KERNEL_SOURCES = ("device_common.hpp", "ew_kernels.hpp", "softmax_kernels.hpp", 
                   "softmax.hip")
 # Kernel-name fragments (as rocprofv3 prints them) of each workload's kernel.
 KERNEL_NAMES = {
-    "C3": ("ew_vec_kernel<fk::IoF32", "ChainOp"),
+    "C3": ("ew_vec_kernel<fk::IoF32", "AffActAffOp"),
     "C4": ("softmax_reg_kernel<fk::IoBF16",),
     "C5a": ("softmax_split_kernel<fk::IoF32",),
     "C5b": ("ew_vec_kernel<fk::IoBF16", "GeluOp"),
@@ -130,9 +130,10 @@ def main() -> int:
     torch.cuda.synchronize()
 
     # C5a rows are wider than one workgroup: the split path exchanges partial
-    # statistics through a zeroed workspace, allocated here once (untimed)
+    # statistics through a caller workspace (any contents), allocated here
+    # once (untimed)
     ws_bytes = fk.fk_softmax_workspace_bytes(*xs["C5a"].shape, xs["C5a"].dtype)
-    ws = torch.zeros(max(ws_bytes, 8), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(ws_bytes, 8), dtype=torch.uint8, device=dev)
     launches = {
         "C3": lambda: fk.fk_elementwise_chain(xs["C3"], ys["C3"], wl.CHAIN_C3),
         "C4": lambda: fk.fk_softmax_rows(xs["C4"], ys["C4"]),
@@ -334,12 +335,20 @@ def measure_extras(fk, wl, torch, xs, ys, stream):
         b.synchronize()
         return a.elapsed_time(b) / reps
 
-    # plain 16-byte copy of the C5b tensor (2 GiB read + 2 GiB written)
+    # copy ceilings at 2 GiB per tensor: this library's 16-byte copy and the
+    # runtime's own device-to-device copy (torch copy_ -> hipMemcpyAsync)
     nbytes = xs["C5b"].numel() * 2
     ms = avg_ms(lambda: fk.fk_copy(xs["C5b"], ys["C5b"], nbytes), 10)
     copy_gbs = 2 * nbytes / (ms * 1e-3) / 1e9
+    rt_ms = avg_ms(lambda: ys["C5b"].copy_(xs["C5b"]), 10)
+    rt_gbs = 2 * nbytes / (rt_ms * 1e-3) / 1e9
     out["copy_ceiling"] = {"bytes": 2 * nbytes, "ms": round(ms, 4), "GBps": round(copy_gbs, 1),
-                           "frac_of_peak": round(copy_gbs / PEAK_HBM_GBS, 4)}
+                           "frac_of_peak": round(copy_gbs / PEAK_HBM_GBS, 4),
+                           "runtime_copy_ms": round(rt_ms, 4),
+                           "runtime_copy_GBps": round(rt_gbs, 1),
+                           "runtime_copy_frac_of_peak": round(rt_gbs / PEAK_HBM_GBS, 4),
+                           "note": "fk_copy and the runtime's device-to-device copy "
+                                   "(hipMemcpyAsync through torch copy_), 2 GiB each way"}
 
     # C3 fused vs the same three ops as three kernels (fp32 intermediates).
     # Each repetition first streams a 2 GiB copy so the 32 MiB operands are
@@ -366,23 +375,17 @@ def measure_extras(fk, wl, torch, xs, ys, stream):
                                 fk.fk_elementwise_chain(t2, t3, ops[2:])))
     fb = wl.algorithmic_bytes("C3")
     ub = wl.algorithmic_bytes("C3", unfused=True)
+    del t1, t2, t3
 
-    # C3 without per-launch event overhead: 16 input/output pairs (1 GiB,
-    # four times the Infinity Cache) launched back to back between two events
-    pairs = [(torch.empty_like(x).copy_(x), torch.empty_like(x)) for _ in range(16)]
-    reps = 64
+    # The small workloads (C1, C2, C3) fit in the 256 MB Infinity Cache:
+    # each is launched back to back over rotating input/output pairs
+    # totalling more than 1 GiB, next to both copies of the same bytes
+    out["rotating_buffers"] = rotating_buffers(fk, wl, torch, stream)
+    out["chain_rotating_buffers"] = out["rotating_buffers"]["C3"]
 
-    def rotating():
-        for k in range(reps):
-            a_, b_ = pairs[k % len(pairs)]
-            fk.fk_elementwise_chain(a_, b_, ops)
-
-    rot_ms = avg_ms(rotating, 1) / reps
-    out["chain_rotating_buffers"] = {
-        "ms": round(rot_ms, 5), "bytes": fb, "GBps": round(fb / (rot_ms * 1e-3) / 1e9, 1),
-        "frac_of_peak": round(fb / (rot_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-        "note": f"{reps} back-to-back launches over 16 rotating 32 MiB input/output pairs"}
-    del pairs
+    # C5a through the online two-pass kernel (fk_softmax_rows without a
+    # workspace takes it too), against the split path of the step
+    out["softmax_online_c5a"] = online_c5a(fk, wl, torch, xs, ys, avg_ms)
 
     # LayerNorm (+ GELU epilogue) on the C4 row shape (bf16 32768 x 4096) and
     # the C2 row shape (fp32 4096 x 1000, rows shifted every 16th); the
@@ -475,7 +478,7 @@ def measure_extras(fk, wl, torch, xs, ys, stream):
     del xl, wlin, bl, yl, xh, wh, bh, yh
 
     # FlashAttention forward on the pages' benchmark grid (B = 4, H = 32,
-    # d = 128, T = 128 ... 4096), against torch's scaled_dot_product_attention
+    # d = 128, T = 128 ... 4096)
     att = {}
     for T in (128, 256, 512, 1024, 2048, 4096):
         qa, ka, va = (wl_.to_torch(wl_.draw(4 * 32 * T * 128, seed=6 + i, dtype="bf16"),
@@ -485,12 +488,9 @@ def measure_extras(fk, wl, torch, xs, ys, stream):
             fl = 4.0 * 4 * 32 * T * T * 128 * (0.5 if causal else 1.0)
             reps = 20 if T <= 1024 else 5
             ms_fk = avg_ms(lambda: fk.fk_attention_fwd(qa, ka, va, oa, causal=causal), reps)
-            ms_lib = avg_ms(lambda: torch.nn.functional.scaled_dot_product_attention(
-                qa, ka, va, is_causal=causal), reps)
             att[f"T{T}_{'causal' if causal else 'full'}"] = {
                 "ms": round(ms_fk, 4), "TFLOPs": round(fl / (ms_fk * 1e-3) / 1e12, 1),
-                "frac_of_mfma_peak": round(fl / (ms_fk * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                "library_sdpa_ms": round(ms_lib, 4)}
+                "frac_of_mfma_peak": round(fl / (ms_fk * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         del qa, ka, va, oa
     # fp16, the dtype the pages benchmark
     for T in (1024, 4096):
@@ -501,12 +501,9 @@ def measure_extras(fk, wl, torch, xs, ys, stream):
             fl = 4.0 * 4 * 32 * T * T * 128 * (0.5 if causal else 1.0)
             reps = 20 if T <= 1024 else 5
             ms_fk = avg_ms(lambda: fk.fk_attention_fwd(qa, ka, va, oa, causal=causal), reps)
-            ms_lib = avg_ms(lambda: torch.nn.functional.scaled_dot_product_attention(
-                qa, ka, va, is_causal=causal), reps)
             att[f"fp16_T{T}_{'causal' if causal else 'full'}"] = {
                 "ms": round(ms_fk, 4), "TFLOPs": round(fl / (ms_fk * 1e-3) / 1e12, 1),
-                "frac_of_mfma_peak": round(fl / (ms_fk * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                "library_sdpa_ms": round(ms_lib, 4)}
+                "frac_of_mfma_peak": round(fl / (ms_fk * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         del qa, ka, va, oa
     out["attention_fwd"] = att
     out["chain_fused_vs_unfused"] = {
@@ -517,6 +514,91 @@ def measure_extras(fk, wl, torch, xs, ys, stream):
         "speedup": round(unfused_ms / fused_ms, 3),
         "pages_traffic_ratio": 3.0,
         "note": "cold Infinity Cache before each measurement"}
+    return out
+
+
+def _median(v):
+    v = sorted(v)
+    n = len(v)
+    return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+
+
+# Rotating-buffer configurations: workload, pairs (input + output per pair;
+# all pairs together hold more than 1 GiB, four times the Infinity Cache)
+ROTATING = (("C1", 160), ("C2", 40), ("C3", 20))
+ROT_GROUPS, ROT_PER_GROUP = 8, 16   # 128 launches per figure
+
+
+def rotating_buffers(fk, wl, torch, stream):
+    """C1, C2 and C3 launched back to back over rotating pairs, next to
+    fk_copy and the runtime's copy of the same bytes, launched alike.
+
+    Each figure times ROT_GROUPS groups of ROT_PER_GROUP back-to-back
+    launches between two events (no event between launches of a group);
+    the per-launch time of a group is its span / ROT_PER_GROUP, and the
+    median and minimum are over the groups (128 launches in all)."""
+    out = {}
+    for name, npairs in ROTATING:
+        x0 = wl.to_torch(wl.make_input(name), "cuda:0")
+        pairs = [(x0.clone(), torch.empty_like(x0)) for _ in range(npairs)]
+        nbytes = x0.numel() * x0.element_size()
+        total = 2 * nbytes * npairs
+        if name == "C1":
+            launch = lambda a, b: fk.fk_gelu_tanh(a, b)  # noqa: E731
+        elif name == "C2":
+            launch = lambda a, b: fk.fk_softmax_rows(a, b)  # noqa: E731
+        else:
+            launch = lambda a, b: fk.fk_elementwise_chain(a, b, wl.CHAIN_C3)  # noqa: E731
+
+        def groups(fn):
+            for k in range(npairs):   # warm-up: every pair once
+                fn(*pairs[k])
+            torch.cuda.synchronize()
+            per = []
+            k = 0
+            for _ in range(ROT_GROUPS):
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for _ in range(ROT_PER_GROUP):
+                    fn(*pairs[k % npairs])
+                    k += 1
+                b.record(stream)
+                b.synchronize()
+                per.append(a.elapsed_time(b) / ROT_PER_GROUP)
+            return per
+
+        t_k = groups(launch)
+        t_c = groups(lambda a, b: fk.fk_copy(a, b, nbytes))
+        t_r = groups(lambda a, b: b.copy_(a))
+        alg = wl.algorithmic_bytes(name)
+        med = _median(t_k)
+        gbs = alg / (med * 1e-3) / 1e9
+        faster_copy = min(_median(t_c), _median(t_r))
+        out[name] = {"median_ms": round(med, 5), "min_ms": round(min(t_k), 5),
+                     "bytes": alg, "GBps": round(gbs, 1),
+                     "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
+                     "fk_copy_median_ms": round(_median(t_c), 5),
+                     "runtime_copy_median_ms": round(_median(t_r), 5),
+                     "frac_of_faster_copy": round(faster_copy / med, 4),
+                     "launches": ROT_GROUPS * ROT_PER_GROUP,
+                     "pairs": npairs, "pair_bytes_total": total}
+        del pairs, x0
+    return out
+
+
+def online_c5a(fk, wl, torch, xs, ys, avg_ms):
+    """C5a (fp32 1024 x 131072) through the online two-pass kernel and
+    through fk_softmax_rows (no workspace: the same online path)."""
+    x, y = xs["C5a"], ys["C5a"]
+    alg = wl.algorithmic_bytes("C5a")
+    out = {"path_without_workspace": fk.fk_softmax_rows_path(x, y)}
+    for key, fn in (("online", lambda: fk.fk_softmax_rows_online(x, y)),
+                    ("fk_softmax_rows", lambda: fk.fk_softmax_rows(x, y))):
+        ms = avg_ms(fn, 20)
+        gbs = alg / (ms * 1e-3) / 1e9
+        out[key] = {"ms": round(ms, 5), "bytes": alg, "GBps": round(gbs, 1),
+                    "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
     return out
 
 

@@ -30,7 +30,7 @@ def test_refuses_bad_step_counts():
 # rocprofv3 kernel names of the counted dispatches (fragments bench.py matches)
 NAMES = {
     "copy": "void fk::copy_vec_kernel<64, 1, true>(unsigned int __vector(4) const*, ...)",
-    "C3": "void fk::ew_vec_kernel<fk::IoF32, 64, 1, true, false, fk::ChainOp>(...)",
+    "C3": "void fk::ew_vec_kernel<fk::IoF32, 64, 1, true, false, fk::AffActAffOp<1, 3, 2> >(...)",
     "C4": "void fk::softmax_reg_kernel<fk::IoBF16, 2, 4, true, true, 2>(...)",
     "C5a": "void fk::softmax_split_kernel<fk::IoF32, 256, 8, true, true>(...)",
     "C5b": "void fk::ew_vec_kernel<fk::IoBF16, 128, 1, true, false, fk::GeluOp>(...)",
