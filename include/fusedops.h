@@ -158,6 +158,28 @@ int fk_softmax_rows_ws(const void* x, void* y, int64_t rows, int64_t cols,
  */
 int64_t fk_softmax_workspace_bytes(int64_t rows, int64_t cols, int dtype);
 
+/*
+ * fk_softmax_rows_ws for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the split path's workspace is the library's own static device
+ * array of FK_SOFTMAX_SCRATCH_BYTES bytes (one per GPU, held until the
+ * process ends) instead of a caller buffer. The call allocates and frees
+ * nothing. Same paths and results as fk_softmax_rows_ws with a large enough
+ * workspace.
+ * Limit: shapes whose split path needs more than FK_SOFTMAX_SCRATCH_BYTES
+ * (fk_softmax_workspace_bytes(rows, cols, dtype) > 1 MiB, e.g. more than
+ * 65536 rows x slices) return FK_ERR_UNSUPPORTED before any HIP call.
+ * Nothing in the array needs clearing (every slot word carries a per-call
+ * tag). Calls that overlap on one GPU (different streams) share the array
+ * and race for its slots: a workgroup whose partials were overwritten waits
+ * out its bound (fk_set_split_wait_limit) and computes its row's statistics
+ * by streaming the row -- correct, but slow. Order such calls on one stream.
+ * FK_ERR_HIP if the array's device address cannot be obtained.
+ */
+#define FK_SOFTMAX_SCRATCH_BYTES (1 << 20)
+int fk_softmax_rows_noalloc(const void* x, void* y, int64_t rows, int64_t cols,
+                            int64_t ldx, int64_t ldy, int dtype, void* stream);
+
 /* Kernel paths of the row softmax. */
 typedef enum {
     FK_PATH_NONE = 0,   /* empty work: nothing launched              */

@@ -38,11 +38,12 @@ FK_ACT_GELU_TANH = 1
 FK_ACT_RELU = 2
 _ACTS = {"none": FK_ACT_NONE, "gelu_tanh": FK_ACT_GELU_TANH, "relu": FK_ACT_RELU}
 FK_MAX_OPS = 8
+FK_SOFTMAX_SCRATCH_BYTES = 1 << 20
 
 __all__ = [
     "FusedOpsError", "lib", "fk_gelu_tanh", "fk_elementwise_chain", "fk_softmax_rows",
     "fk_softmax_rows_online", "fk_softmax_rows_ws", "fk_softmax_workspace_bytes",
-    "fk_softmax_rows_path",
+    "fk_softmax_rows_path", "fk_softmax_rows_noalloc", "FK_SOFTMAX_SCRATCH_BYTES",
     "fk_set_split_wait_limit", "fk_softmax_onchip_max_cols", "fk_layernorm_rows",
     "fk_layernorm_max_cols", "fk_copy", "fk_status_string", "layernorm_rows",
     "fk_gelu_tanh_backward", "fk_softmax_rows_backward", "fk_softmax_backward_max_cols",
@@ -87,6 +88,8 @@ def lib() -> ctypes.CDLL:
         fn.restype = i32
     L.fk_softmax_rows_ws.argtypes = [vp, vp, i64, i64, i64, i64, i32, vp, i64, vp]
     L.fk_softmax_rows_ws.restype = i32
+    L.fk_softmax_rows_noalloc.argtypes = [vp, vp, i64, i64, i64, i64, i32, vp]
+    L.fk_softmax_rows_noalloc.restype = i32
     L.fk_softmax_rows_path.argtypes = [vp, vp, i64, i64, i64, i64, i32, i64]
     L.fk_softmax_rows_path.restype = i32
     L.fk_softmax_workspace_bytes.argtypes = [i64, i64, i32]
@@ -279,6 +282,18 @@ def _dtype_arg(dtype) -> int:
         return dtype
     torch = _torch()
     return {torch.float32: FK_F32, torch.bfloat16: FK_BF16, torch.float16: FK_F16}.get(dtype, -1)
+
+
+def fk_softmax_rows_noalloc(x, y, stream=None) -> None:
+    """As fk_softmax_rows_ws, with the library's static device scratch as the
+    split path's workspace: no allocation at all (FusedOpsError with
+    FK_ERR_UNSUPPORTED when the shape needs more than
+    FK_SOFTMAX_SCRATCH_BYTES)."""
+    rows, cols, ldx, ldy, dt = _rows_pair(x, y, "fk_softmax_rows_noalloc")
+    with _on_device(x):
+        _check(lib().fk_softmax_rows_noalloc(x.data_ptr(), y.data_ptr(), rows, cols, ldx, ldy, dt,
+                                             _stream_handle(x, stream)),
+               "fk_softmax_rows_noalloc")
 
 
 def fk_softmax_rows_path(x, y, workspace_bytes: int = 0) -> int:

@@ -11,6 +11,7 @@ static_assert(FK_MAX_OPS == fk::kMaxOps, "op list size mismatch");
 static_assert(int(FK_OP_ADD_SCALAR) == int(fk::kOpAdd) && int(FK_OP_MUL_SCALAR) == int(fk::kOpMul) &&
                   int(FK_OP_GELU_TANH) == int(fk::kOpGelu) && int(FK_OP_RELU) == int(fk::kOpRelu),
               "op kind mismatch");
+static_assert(FK_SOFTMAX_SCRATCH_BYTES == fk::kSoftmaxScratchBytes, "scratch size mismatch");
 static_assert(int(FK_PATH_ONCHIP) == int(fk::kPathOnChip) &&
                   int(FK_PATH_SPLIT) == int(fk::kPathSplit) &&
                   int(FK_PATH_ONLINE) == int(fk::kPathOnline),
@@ -157,6 +158,21 @@ int fk_softmax_rows_ws(const void* x, void* y, int64_t rows, int64_t cols, int64
     if (st != FK_OK) return st;
     return softmax_launch(x, y, rows, cols, ldx, ldy, dtype, false, workspace, workspace_bytes,
                           stream);
+}
+
+int fk_softmax_rows_noalloc(const void* x, void* y, int64_t rows, int64_t cols, int64_t ldx,
+                            int64_t ldy, int dtype, void* stream) {
+    bool skip = false;
+    const int st = check_rows(x, y, rows, cols, ldx, ldy, dtype, &skip);
+    if (st != FK_OK || skip) return st;
+    const int64_t need = x == y ? 0 : fk::softmax_workspace_bytes(rows, cols, static_cast<fk::Dtype>(dtype));
+    if (need > fk::kSoftmaxScratchBytes) return FK_ERR_UNSUPPORTED;
+    void* ws = nullptr;
+    if (need > 0) {
+        const hipError_t e = fk::softmax_scratch(&ws);
+        if (e != hipSuccess) return FK_ERR_HIP;
+    }
+    return softmax_launch(x, y, rows, cols, ldx, ldy, dtype, false, ws, need, stream);
 }
 
 int fk_softmax_rows_path(const void* x, const void* y, int64_t rows, int64_t cols, int64_t ldx,

@@ -39,6 +39,10 @@ SoftmaxPath softmax_path(int64_t rows, int64_t cols, Dtype dt, bool in_place, bo
 int64_t softmax_onchip_max_cols(Dtype dt);
 // Workspace the split path needs for this shape; 0 if it does not apply.
 int64_t softmax_workspace_bytes(int64_t rows, int64_t cols, Dtype dt);
+// The library's static split-path scratch on the current device (address
+// looked up once per device); kSoftmaxScratchBytes bytes, any contents.
+constexpr int64_t kSoftmaxScratchBytes = int64_t(1) << 20;
+hipError_t softmax_scratch(void** ptr);
 // Bound on the polls of a split-kernel block waiting for its row's other
 // slices; past it the block computes the row statistics itself.
 int64_t split_wait_limit();

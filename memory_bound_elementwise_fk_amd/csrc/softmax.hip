@@ -2,7 +2,7 @@
 // the single-pass kernel for rows up to the on-chip capacity; above it the
 // split kernel when the caller brings a workspace, else the online kernel.
 #include <atomic>
-
+#include <mutex>
 #include <utility>
 
 #include "launch.hpp"
@@ -208,7 +208,37 @@ hipError_t launch_softmax_t(const void* x, void* y, int64_t rows, int64_t cols, 
     return launch_online<IO>(x, y, rows, cols, ldx, ldy, vec, s);
 }
 
+// The split path's slots for callers that cannot allocate: a file-scope
+// device array (each GPU the library runs on holds its own copy until the
+// process ends). Host code never uses the symbol itself -- on the host it is
+// a stand-in, not a device address -- but the address hipGetSymbolAddress
+// returns for the current device, looked up once per device.
+static __device__ __align__(256) unsigned char scratch[kSoftmaxScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
 }  // namespace
+
+hipError_t softmax_scratch(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return hipSuccess;
+}
 
 int64_t softmax_onchip_max_cols(Dtype dt) {
     return dt == kF32 ? reg_capacity<IoF32>(kRegShapes[kNumRegShapes - 1])
