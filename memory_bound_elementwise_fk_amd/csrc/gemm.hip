@@ -1,4 +1,6 @@
 // gemm.hip -- launcher of the Linear + GELU kernel (gemm_kernels.hpp).
+#include <limits>
+
 #include "gemm_kernels.hpp"
 #include "launch.hpp"
 
@@ -27,8 +29,14 @@ int64_t linear_max_tiles() {
                                                                             : LinearDtlShape::kThreads);
 }
 
+// Output tiles of an M x N product (M, N >= 0), saturating at INT64_MAX
+// instead of overflowing for sizes the caller will refuse anyway.
 int64_t linear_tiles(int64_t M, int64_t N) {
-    return ((M + LinearShape::BM - 1) / LinearShape::BM) * ((N + LinearShape::BN - 1) / LinearShape::BN);
+    const int64_t tm = M / LinearShape::BM + (M % LinearShape::BM != 0);
+    const int64_t tn = N / LinearShape::BN + (N % LinearShape::BN != 0);
+    if (tm != 0 && tn > std::numeric_limits<int64_t>::max() / tm)
+        return std::numeric_limits<int64_t>::max();
+    return tm * tn;
 }
 
 hipError_t launch_linear_gelu(const void* x, const void* w, const void* bias, void* y, int64_t M,

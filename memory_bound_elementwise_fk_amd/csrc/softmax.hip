@@ -147,9 +147,9 @@ uint32_t next_split_epoch() {
 
 template <class IO>
 int64_t split_parts(int64_t rows, int64_t cols) {
-    const int64_t parts = (cols + kSplitWidth<IO> - 1) / kSplitWidth<IO>;
     if (cols <= reg_capacity<IO>(kRegShapes[kNumRegShapes - 1])) return 0;  // on-chip path
-    if (parts > kSplitMaxParts) return 0;
+    if (cols > kSplitMaxParts * kSplitWidth<IO>) return 0;  // more than 64 slices
+    const int64_t parts = (cols + kSplitWidth<IO> - 1) / kSplitWidth<IO>;  // (no overflow now)
     if (rows > (kMaxWorkItems / kSplitThreads) / parts) return 0;  // one block per slice
     return parts;
 }
