@@ -526,17 +526,20 @@ def _median(v):
 # Rotating-buffer configurations: workload, pairs (input + output per pair;
 # all pairs together hold more than 1 GiB, four times the Infinity Cache)
 ROTATING = (("C1", 160), ("C2", 40), ("C3", 20))
-ROT_GROUPS, ROT_PER_GROUP = 8, 16   # 128 launches per figure
+ROT_REPLAYS = 8   # replays of the graph of one launch per pair
 
 
 def rotating_buffers(fk, wl, torch, stream):
     """C1, C2 and C3 launched back to back over rotating pairs, next to
     fk_copy and the runtime's copy of the same bytes, launched alike.
 
-    Each figure times ROT_GROUPS groups of ROT_PER_GROUP back-to-back
-    launches between two events (no event between launches of a group);
-    the per-launch time of a group is its span / ROT_PER_GROUP, and the
-    median and minimum are over the groups (128 launches in all)."""
+    One launch per pair is captured into a HIP graph (so the launches are
+    not bound by the host's per-call cost: C1 takes ~4.5 us on the device,
+    about what one call through the binding costs on the host); the graph
+    is replayed ROT_REPLAYS times between events, and a replay's span /
+    pairs is one launch's time. Median and minimum are over the replays
+    (8 x pairs launches: 1280 for C1, 320 for C2, 160 for C3). If capture
+    is unavailable the same launches run eagerly."""
     out = {}
     for name, npairs in ROTATING:
         x0 = wl.to_torch(wl.make_input(name), "cuda:0")
@@ -550,27 +553,42 @@ def rotating_buffers(fk, wl, torch, stream):
         else:
             launch = lambda a, b: fk.fk_elementwise_chain(a, b, wl.CHAIN_C3)  # noqa: E731
 
-        def groups(fn):
-            for k in range(npairs):   # warm-up: every pair once
-                fn(*pairs[k])
+        def per_launch_ms(fn):
+            def all_pairs():
+                for a, b in pairs:
+                    fn(a, b)
+
+            all_pairs()  # warm-up (and first-call setup) outside the capture
             torch.cuda.synchronize()
+            replay, how = all_pairs, "eager"
+            try:
+                g = torch.cuda.CUDAGraph()
+                side = torch.cuda.Stream()
+                side.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(side):
+                    with torch.cuda.graph(g, stream=side):
+                        all_pairs()
+                torch.cuda.current_stream().wait_stream(side)
+                replay, how = g.replay, "graph"
+                replay()
+                torch.cuda.synchronize()
+            except Exception as exc:  # noqa: BLE001
+                log(f"{name}: graph capture unavailable ({exc}); eager launches")
+                torch.cuda.synchronize()
             per = []
-            k = 0
-            for _ in range(ROT_GROUPS):
+            for _ in range(ROT_REPLAYS):
                 a = torch.cuda.Event(enable_timing=True)
                 b = torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                for _ in range(ROT_PER_GROUP):
-                    fn(*pairs[k % npairs])
-                    k += 1
-                b.record(stream)
+                a.record()
+                replay()
+                b.record()
                 b.synchronize()
-                per.append(a.elapsed_time(b) / ROT_PER_GROUP)
-            return per
+                per.append(a.elapsed_time(b) / npairs)
+            return per, how
 
-        t_k = groups(launch)
-        t_c = groups(lambda a, b: fk.fk_copy(a, b, nbytes))
-        t_r = groups(lambda a, b: b.copy_(a))
+        t_k, how = per_launch_ms(launch)
+        t_c, _ = per_launch_ms(lambda a, b: fk.fk_copy(a, b, nbytes))
+        t_r, _ = per_launch_ms(lambda a, b: b.copy_(a))
         alg = wl.algorithmic_bytes(name)
         med = _median(t_k)
         gbs = alg / (med * 1e-3) / 1e9
@@ -581,7 +599,7 @@ def rotating_buffers(fk, wl, torch, stream):
                      "fk_copy_median_ms": round(_median(t_c), 5),
                      "runtime_copy_median_ms": round(_median(t_r), 5),
                      "frac_of_faster_copy": round(faster_copy / med, 4),
-                     "launches": ROT_GROUPS * ROT_PER_GROUP,
+                     "launches": ROT_REPLAYS * npairs, "launched_as": how,
                      "pairs": npairs, "pair_bytes_total": total}
         del pairs, x0
     return out

@@ -226,3 +226,26 @@ def test_layernorm_rows_beyond_one_launch_grid(cols):
     torch.cuda.empty_cache()
     assert_ln(ys, oracle.layernorm_rows(xs, g, b, gelu=True), "f32", cols, g, b, True,
               f"layernorm {rows}x{cols}, sampled rows")
+
+
+# More row groups than the launch's workgroup cap: each workgroup strides
+# over many rows (several rows per workgroup on narrow shapes), alternating
+# its reduction slots; odd row counts leave a partial last step.
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("cols", [64, 1000])
+def test_layernorm_many_rows_grid_strided(dt, cols):
+    rows = 70001
+    x = random_input((rows, cols), dt, 2.0, seed=cols + 7)
+    rng = np.random.default_rng(cols)
+    g = (1.0 + 0.25 * rng.standard_normal(cols)).astype(np.float32)
+    b = (0.5 * rng.standard_normal(cols)).astype(np.float32)
+    if dt == "bf16":
+        g, b = wl.f32_to_bf16_bits(g), wl.f32_to_bf16_bits(b)
+    xt = to_dev(x)
+    full, y = guarded(x.shape, tdtype(dt))
+    fk.fk_layernorm_rows(xt, y, to_dev(g), to_dev(b), gelu=True)
+    got = to_host(y)
+    assert guards_intact(full, x.size)
+    assert_ln(got, oracle.layernorm_rows(x, g, b, gelu=True, threads=T), dt, cols,
+              g if dt == "f32" else oracle.bf16_to_f32(g),
+              b if dt == "f32" else oracle.bf16_to_f32(b), True, f"ln {dt} {rows}x{cols}")
