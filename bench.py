@@ -52,13 +52,15 @@ KERNEL_NAMES = {
     "layernorm_gelu": ("layernorm_reg_kernel<fk::IoBF16",),
     "gelu_backward": ("ew2_vec_kernel<fk::IoBF16", "GeluBwdOp"),
     "softmax_backward": ("softmax_bwd_reg_kernel<fk::IoBF16",),
+    "online_c5a": ("softmax_staged_kernel<fk::IoF32",),
 }
 # Next-row kernels in the counter run (bytes per launch: one read of each
 # input, one write of the output; gamma and beta of the LayerNorm once).
-EXTRA = ("layernorm_gelu", "gelu_backward", "softmax_backward")
+EXTRA = ("layernorm_gelu", "gelu_backward", "softmax_backward", "online_c5a")
 EXTRA_BYTES = {"layernorm_gelu": 2 * 32768 * 4096 * 2 + 2 * 4096 * 2,
                "gelu_backward": 3 * (1 << 30) * 2,
-               "softmax_backward": 3 * 32768 * 4096 * 2}
+               "softmax_backward": 3 * 32768 * 4096 * 2,
+               "online_c5a": 2 * 1024 * 131072 * 4}
 CPU_BASELINE_MIN_SECONDS = 10.0
 
 
@@ -85,6 +87,11 @@ def parse():
     ap.add_argument("--counters-run", action="store_true",
                     help="launch each kernel of the step twice plus a 1 GiB calibration copy, "
                          "nothing else (for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE passes)")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="launch each next-row kernel twice on the extras' shapes (Linear + GELU "
+                         "bf16 8192x16384x4096, attention B4 H32 T4096 d128 full and causal, "
+                         "LayerNorm + GELU bf16 32768x4096, C5a through the online path), "
+                         "nothing else (for rocprofv3 --pmc passes of SQ counters)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn the two rocprofv3 counter_collection.csv files of a "
                          "--counters-run into profiles/traffic.json and exit")
@@ -142,6 +149,8 @@ def main() -> int:
     }
     if args.counters_run:
         return counters_run(fk, torch, launches, xs, ys)
+    if args.profile_run:
+        return profile_run(fk, torch, xs, ys)
     kbytes = {name: wl.algorithmic_bytes(name) for name in STEP}
     step_bytes = sum(kbytes.values())
 
@@ -678,8 +687,8 @@ def cpu_baseline(host, kbytes):
 
 def counters_run(fk, torch, launches, xs, ys):
     """Each step kernel twice and one 1 GiB copy, for per-dispatch counters;
-    then twice each of the LayerNorm + GELU, GELU backward and softmax
-    backward launches the extras time (same shapes)."""
+    then twice each of the LayerNorm + GELU, GELU backward, softmax backward
+    and online-path C5a launches the extras time (same shapes)."""
     calib = 1 << 30
     a = torch.empty(calib, dtype=torch.uint8, device="cuda:0")
     b = torch.empty_like(a)
@@ -696,6 +705,33 @@ def counters_run(fk, torch, launches, xs, ys):
     torch.cuda.synchronize()
     log(f"counters run done: calibration copy {calib} B, then 2 x {', '.join(STEP)}, "
         f"then 2 x {', '.join(EXTRA)}")
+    return 0
+
+
+def profile_run(fk, torch, xs, ys):
+    """Two launches each of the next-row kernels on the extras' shapes."""
+    from memory_bound_elementwise_fk_amd import workloads as wl
+
+    M, N, K = 8192, 16384, 4096
+    xl = wl.to_torch(wl.draw(M * K, seed=3, dtype="bf16"), "cuda:0").view(M, K)
+    wlin = wl.to_torch(wl.draw(N * K, seed=4, scale=K ** -0.5, dtype="bf16"), "cuda:0").view(N, K)
+    bl = wl.to_torch(wl.draw(N, seed=5, dtype="bf16"), "cuda:0")
+    yl = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+    T = 4096
+    qa, ka, va = (wl.to_torch(wl.draw(4 * 32 * T * 128, seed=6 + i, dtype="bf16"),
+                              "cuda:0").view(4, 32, T, 128) for i in range(3))
+    oa = torch.empty_like(qa)
+    extra = extra_launches(fk, torch, xs, ys)
+    runs = [("linear_gelu", lambda: fk.fk_linear_gelu(xl, wlin, bl, yl)),
+            ("attention_full", lambda: fk.fk_attention_fwd(qa, ka, va, oa, causal=False)),
+            ("attention_causal", lambda: fk.fk_attention_fwd(qa, ka, va, oa, causal=True)),
+            ("layernorm_gelu", extra["layernorm_gelu"]),
+            ("online_c5a", lambda: fk.fk_softmax_rows_online(xs["C5a"], ys["C5a"]))]
+    for name, fn in runs:
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        log(f"profile run: 2 x {name}")
     return 0
 
 
@@ -722,6 +758,7 @@ def extra_launches(fk, torch, xs, ys):
         "layernorm_gelu": lambda: fk.fk_layernorm_rows(xb, yb, gb, bb, gelu=True),
         "gelu_backward": lambda: fk.fk_gelu_tanh_backward(xs["C5b"], ys["C5b"], dx5),
         "softmax_backward": lambda: fk.fk_softmax_rows_backward(ys["C4"], xs["C4"], dx4),
+        "online_c5a": lambda: fk.fk_softmax_rows_online(xs["C5a"], ys["C5a"]),
     }
 
 
