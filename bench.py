@@ -62,6 +62,7 @@ EXTRA_BYTES = {"layernorm_gelu": 2 * 32768 * 4096 * 2 + 2 * 4096 * 2,
                "softmax_backward": 3 * 32768 * 4096 * 2,
                "online_c5a": 2 * 1024 * 131072 * 4}
 CPU_BASELINE_MIN_SECONDS = 10.0
+WARM_SECONDS = 0.1      # launches before each extras measurement (clocks up)
 
 
 def kernel_source_hash() -> str:
@@ -334,9 +335,16 @@ def measure_extras(fk, wl, torch, xs, ys, stream):
     out = {}
 
     def avg_ms(fn, reps):
+        # warm up for ~0.1 s of launches first: each measurement here follows
+        # host-side input generation, during which the GPU idles and its
+        # clocks drop (a single warm-up launch left some kernels 5-10 % slow)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        fn()
-        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(2000):
+            fn()
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 > WARM_SECONDS:
+                break
         a.record(stream)
         for _ in range(reps):
             fn()
@@ -583,6 +591,10 @@ def rotating_buffers(fk, wl, torch, stream):
                 torch.cuda.synchronize()
             except Exception as exc:  # noqa: BLE001
                 log(f"{name}: graph capture unavailable ({exc}); eager launches")
+                torch.cuda.synchronize()
+            t0 = time.perf_counter()   # clocks up before the timed replays
+            while time.perf_counter() - t0 < WARM_SECONDS:
+                replay()
                 torch.cuda.synchronize()
             per = []
             for _ in range(ROT_REPLAYS):

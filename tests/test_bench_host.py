@@ -37,6 +37,7 @@ NAMES = {
     "layernorm_gelu": "void fk::layernorm_reg_kernel<fk::IoBF16, 4, 2, true, true, true, 2>(...)",
     "gelu_backward": "void fk::ew2_vec_kernel<fk::IoBF16, 128, true, false, fk::GeluBwdOp>(...)",
     "softmax_backward": "void fk::softmax_bwd_reg_kernel<fk::IoBF16, 2, 4, true, true, 2>(...)",
+    "online_c5a": "void fk::softmax_staged_kernel<fk::IoF32, 512, 4, 12, 4, true>(...)",
 }
 
 
@@ -72,6 +73,8 @@ def test_ingest_counters_scales_by_the_calibration_copy(tmp_path, monkeypatch):
             written = 2 * 32768 * 4096 if name != "gelu_backward" else 2 * (1 << 30)
             if name == "layernorm_gelu":
                 written = 32768 * 4096 * 2
+            if name == "online_c5a":
+                written = 1024 * 131072 * 4
             fetch.append((d, NAMES[name], (total - written) / 1024 / 2))
             write.append((d, NAMES[name], written / 1024))
             d += 1
