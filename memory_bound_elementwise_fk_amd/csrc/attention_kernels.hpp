@@ -53,6 +53,7 @@ constexpr int kAttnBlockBytes = kAttnBC * kAttnRowBytes;        // 16 KiB per op
 // direct loads per wave, per operand and block (each fills 1 KiB = 4 rows)
 constexpr int kAttnDmaPerWave = kAttnBlockBytes / 1024 / kAttnWaves;
 static_assert(kAttnDmaPerWave * 1024 * kAttnWaves == kAttnBlockBytes, "whole wave loads");
+static_assert(kAttnDmaPerWave == 4, "the staging offsets take a wave's rows as 16 w + 4 j + drow");
 // LDS layout of a block: row r (key) holds its 16 chunks of 16 bytes (8
 // dims each) permuted, chunk c at position c ^ swz(r): K with r % 16 (the
 // S^T fragment reads, 16 consecutive keys of one chunk per 256 bytes, hit
@@ -91,11 +92,10 @@ __device__ inline u32x2 lds_read_tr16(const uint16_t* p) {
     return __builtin_bit_cast(u32x2, r);
 }
 
-// Two waves per SIMD (two workgroups per CU; LDS 70 KiB each): with one, a
+// Two waves per SIMD (two workgroups per CU; LDS 64 KiB each): with one, a
 // wave's MFMA, exponential and LDS phases run back to back and the K/V loads
-// barely overlap them; the second workgroup fills those gaps. The compiler
-// fits the kernel in 256 registers (no AGPRs) when asked to, spilling a few
-// load offsets that are reloaded outside the MFMA phases.
+// barely overlap them; the second workgroup fills those gaps. The kernel
+// fits in the 256 registers (no AGPRs) this leaves a wave.
 template <class EL, bool WIDE>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attention_fwd_kernel(AttnArgs a) {  // EL: MmaBF16 or MmaF16
@@ -145,11 +145,16 @@ void attention_fwd_kernel(AttnArgs a) {  // EL: MmaBF16 or MmaF16
 
     // Staging: wave w's direct load j of a block fills rows 4 (4 w + j) ..
     // + 3 of K (and of V); lane i writes position i % 16 of row i / 16 of
-    // those, so it fetches the logical chunk at that position. The lane's
-    // source offsets within a block are fixed (kept per load); a block wholly
-    // inside T adds its first row, the last partial one clamps rows past T to
-    // row T - 1 (valid memory; those keys are masked, p = 0). LDS addresses
-    // are wave-uniform (scalar).
+    // those, so it fetches the logical chunk at that position. Row
+    // r = 16 w + 4 j + drow has r % 16 = 4 j + drow and r % 4 = drow, so the
+    // lane's source offset within a block is, for K,
+    // (16 w + 4 j) kt + drow kt + ((dpos ^ drow) 8 ^ 32 j) and, for V,
+    // (16 w + 4 j) vt + drow vt + (dpos ^ 4 drow) 8: three lane values for
+    // the eight loads (kept per load they took eight registers, which the
+    // kernel's 256 could not spare). A block wholly inside T adds its first
+    // row; the last partial one clamps rows past T to row T - 1 (valid
+    // memory; those keys are masked, p = 0). LDS addresses are wave-uniform
+    // (scalar).
     const int drow = lane / 16, dpos = lane % 16;
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     const uint32_t ks_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((las_ptr)(&Ks[0][0])));
@@ -157,13 +162,9 @@ void attention_fwd_kernel(AttnArgs a) {  // EL: MmaBF16 or MmaF16
     // element offsets within a block: 32-bit unless 64 rows of a stride
     // exceed 2^31 elements (WIDE, chosen on the host)
     typedef typename std::conditional<WIDE, int64_t, int32_t>::type off_t;
-    off_t koff[kAttnDmaPerWave], voff[kAttnDmaPerWave];
-#pragma unroll
-    for (int j = 0; j < kAttnDmaPerWave; ++j) {
-        const int r = (wave * kAttnDmaPerWave + j) * 4 + drow;
-        koff[j] = static_cast<off_t>(r * a.kt + (dpos ^ attn_swz_k(r)) * 8);
-        voff[j] = static_cast<off_t>(r * a.vt + (dpos ^ attn_swz_v(r)) * 8);
-    }
+    const off_t k_row = static_cast<off_t>(drow * a.kt);
+    const int k_chunk = (dpos ^ drow) * 8;
+    const off_t v_lane = static_cast<off_t>(drow * a.vt + (dpos ^ attn_swz_v(drow)) * 8);
     // the block at key kb0 of K (IS_V false) or V into buffer buf
     auto issue = [&](bool is_v, int64_t kb0, int buf) {
         const bool whole = kb0 + kAttnBC <= a.T;
@@ -174,7 +175,9 @@ void attention_fwd_kernel(AttnArgs a) {  // EL: MmaBF16 or MmaF16
 #pragma unroll
         for (int j = 0; j < kAttnDmaPerWave; ++j) {
             const uint32_t off = static_cast<uint32_t>((wave_s * kAttnDmaPerWave + j) * 1024);
-            const uint16_t* src = blk + (is_v ? voff[j] : koff[j]);
+            const off_t rows0 = static_cast<off_t>((wave_s * kAttnDmaPerWave + j) * 4 * st);
+            const uint16_t* src =
+                blk + rows0 + (is_v ? v_lane : static_cast<off_t>(k_row + (k_chunk ^ (32 * j))));
             if (!whole) {
                 const int r = (wave * kAttnDmaPerWave + j) * 4 + drow;
                 const int64_t key = kb0 + r < a.T ? kb0 + r : a.T - 1;
