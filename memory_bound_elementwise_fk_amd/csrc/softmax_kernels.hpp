@@ -386,7 +386,7 @@ __global__ __launch_bounds__(THREADS) void softmax_online_kernel(
 
 // ---------------------------------------------------------- staged kernel -
 // The online two-pass kernel for 16-byte-aligned rows, keeping as much of the
-// row on chip as a 1024-lane workgroup can hold, so that only the rest is
+// row on chip as a 512-lane workgroup can hold, so that only the rest is
 // read from HBM twice. The row is cut into chunks of THREADS * VPL 16-byte
 // vectors (one vector per lane per k < VPL, the layout of load_span); chunk
 // c < RREG stays in the lanes' VGPRs as raw 16-byte words, chunk
@@ -400,10 +400,10 @@ __global__ __launch_bounds__(THREADS) void softmax_online_kernel(
 // to be in L2 or the Infinity Cache), the resident ones come from VGPRs and
 // LDS. Each resident element is read from HBM once and written once.
 //
-// With the launcher's shapes (16384-column chunks; fp32: RREG 5, RLDS 2,
-// bf16: RREG 8, RLDS 4) 114688 fp32 columns (448 KiB) or 196608 bf16
-// columns (384 KiB) stay on chip: a 1024 x 131072 fp32 row re-reads one
-// chunk in eight.
+// With the launcher's shapes (8192-column chunks, two waves per SIMD at 256
+// VGPRs; fp32: VPL 4, RREG 12, RLDS 4; bf16: VPL 2, RREG 24, RLDS 8) the
+// first 131072 fp32 or 262144 bf16 columns (512 KiB) stay on chip: a
+// 1024 x 131072 fp32 row is read from HBM once.
 template <class IO, int VPL, int LANES, bool NT>
 __device__ inline void load_raw_span(const char* xr, int64_t cols, int64_t c0, int lane,
                                      u32x4 (&w)[VPL]) {
