@@ -107,7 +107,7 @@ def test_linear_without_bias_and_k_zero():
     assert np.array_equal(to_host(ye), np.broadcast_to(oracle.gelu_tanh(b), (5, 70)))
 
 
-@pytest.mark.parametrize("K", [136, 160])  # register-staged / direct-to-LDS kernel
+@pytest.mark.parametrize("K", [136, 160, 192])  # register-staged / direct-to-LDS kernel
 def test_linear_strided_operands(K):
     M, N = 300, 260
     x, w, b = operands(M, N, K, seed=5)
@@ -131,6 +131,26 @@ def test_linear_mlp_shape_sampled_rows(dt):
     rows = np.sort(np.random.default_rng(10).choice(M, 48, replace=False))
     got = to_host(y[torch.from_numpy(rows).to(DEV)])
     check(got, x, w, b, True, f"{dt} 8192x16384x4096 sampled rows", rows=rows)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
+def test_linear_unaligned_bias_and_output(dt):
+    # bias one element past an aligned address and an output row stride that
+    # is not a multiple of 4, with M and N ragged against the 256 x 256 tiles
+    M, N, K = 300, 270, 128
+    x, w, b = operands(M, N, K, seed=21, dt=dt)
+    bpad = np.zeros(N + 1, b.dtype)
+    bpad[1:] = b
+    bdev = to_dev(bpad)[1:]
+    assert bdev.data_ptr() % 8 != 0
+    tdt = torch.float16 if dt == "fp16" else torch.bfloat16
+    ybuf = torch.full((M, N + 1), 0x7FC1 if dt == "bf16" else 0x7E01, dtype=torch.int16,
+                      device=DEV).view(tdt)
+    fk.fk_linear_gelu(to_dev(x), to_dev(w), bdev, ybuf[:, :N])
+    got = to_host(ybuf)
+    check(got[:, :N], x, w, b, True, f"{dt} unaligned bias/output")
+    pad = np.ascontiguousarray(got[:, N:]).view(np.uint16)
+    assert np.all(pad == (0x7FC1 if dt == "bf16" else 0x7E01)), "row padding of y was written"
 
 
 def test_linear_is_bitwise_reproducible():
