@@ -298,8 +298,8 @@ typedef enum {
  * w: N rows of K (a Linear weight, row stride ldw), bias: N values or NULL,
  * y: M rows of N (row stride ldy); all DEVICE memory of dtype. fp32
  * accumulation; y rounded once to the dtype (nearest even).
- * Supported: dtype FK_BF16 or FK_F16; K, ldx and ldw multiples of 8; x and w
- * 16-byte aligned -- else FK_ERR_UNSUPPORTED. y must not overlap x, w or
+ * Supported: dtype FK_BF16 or FK_F16; K < 2^36, and K, ldx and ldw
+ * multiples of 8; x and w 16-byte aligned -- else FK_ERR_UNSUPPORTED. y must not overlap x, w or
  * bias (FK_ERR_OVERLAP). M == 0 or N == 0: nothing to do. K == 0 gives
  * GELU(bias).
  */

@@ -307,7 +307,7 @@ void linear_gelu_dtl_kernel(const uint16_t* __restrict__ X, const uint16_t* __re
             src[j] = W + row * ldw + lchunk * 8;
         }
     }
-    auto issue = [&](int64_t kt) {  // loads of K step kt into stage kt % kStages
+    auto issue = [&](int kt) {  // loads of K step kt into stage kt % kStages
         char* stage = smem + (kt % S::kStages) * S::kStageBytes;
 #pragma unroll
         for (int j = 0; j < S::kLoadsPerWave; ++j) {
@@ -325,14 +325,23 @@ void linear_gelu_dtl_kernel(const uint16_t* __restrict__ X, const uint16_t* __re
 #pragma unroll
         for (int j = 0; j < S::kTN; ++j) acc[i][j] = f32x16{};
 
-    const int64_t nk = K / S::BK;
+    // 32-bit step counters (the host refuses K >= 2^36), and what only the
+    // epilogue needs (M, N, ldy, the bias and output pointers) carried across
+    // the main loop as lane values (an empty asm makes them opaque): 64-bit
+    // step counters and those scalars kept live through the loop filled the
+    // SGPR budget, and the compiler spilled 24 SGPRs to VGPR lanes
+    const int nk = static_cast<int>(K / S::BK);
+    int64_t Mv = M, Nv = N, ldyv = ldy;
+    const uint16_t* biasv = bias;
+    uint16_t* Yv = Y;
+    asm volatile("" : "+v"(Mv), "+v"(Nv), "+v"(ldyv), "+v"(biasv), "+v"(Yv));
 #pragma unroll
     for (int st = 0; st < S::kStages - 1; ++st)
         if (st < nk) issue(st);
 
     // fragment rows of this lane and the swizzled chunk offsets per kk
     const int frow = lane % 32;
-    for (int64_t kt = 0; kt < nk; ++kt) {
+    for (int kt = 0; kt < nk; ++kt) {
         // stage kt landed: at most (kStages - 2) later steps' loads in flight
         if (kt + S::kStages - 2 < nk)
             __builtin_amdgcn_s_waitcnt(vmcnt_imm((S::kStages - 2) * S::kLoadsPerWave));
@@ -367,10 +376,11 @@ void linear_gelu_dtl_kernel(const uint16_t* __restrict__ X, const uint16_t* __re
     }
 
     // epilogue: + bias, the activation on the accumulators, round, store
+    const int64_t ldy5 = 5 * ldyv;
 #pragma unroll
     for (int j = 0; j < S::kTN; ++j) {
         const int64_t col = n0 + wn * S::WN + j * 32 + lane % 32;
-        const float bv = (bias != nullptr && col < N) ? EL::load1(bias, col) : 0.0f;
+        const float bv = (biasv != nullptr && col < Nv) ? EL::load1(biasv, col) : 0.0f;
 #pragma unroll
         for (int i = 0; i < S::kTM; ++i) {
             float v[16];
@@ -382,11 +392,16 @@ void linear_gelu_dtl_kernel(const uint16_t* __restrict__ X, const uint16_t* __re
 #pragma unroll
                 for (int e = 0; e < 16; ++e) v[e] = relu1(v[e]);
             }
+            // rows row0 + (e / 4) * 8 + e % 4, reached by stepping one
+            // pointer (scalar strides) rather than by 16 row products, whose
+            // 64-bit scalars would spill the SGPRs
             const int64_t row0 = m0 + wm * S::WM + i * 32 + (lane / 32) * 4;
+            const int64_t left = Mv - row0;
+            uint16_t* p = Yv + row0 * ldyv + col;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int64_t row = row0 + (e / 4) * 8 + e % 4;
-                if (row < M && col < N) EL::store1(Y, row * ldy + col, v[e]);
+                if ((e / 4) * 8 + e % 4 < left && col < Nv) EL::store1(p, 0, v[e]);
+                p += (e % 4 == 3) ? ldy5 : ldyv;
             }
         }
     }

@@ -271,6 +271,9 @@ def test_linear_validation(L):
     assert f(A + 2, B, None, Y, 4, 10, 16, 16, 16, 10, 1, bf, None) == fk.FK_ERR_UNSUPPORTED
     assert f(A, B, None, A + 32, 4, 10, 16, 16, 16, 10, 1, bf, None) == fk.FK_ERR_OVERLAP
     assert f(A, B, Y + 4, Y, 4, 10, 16, 16, 16, 10, 1, bf, None) == fk.FK_ERR_OVERLAP
+    # K steps of 32 are counted in 32 bits: K >= 2^36 is refused before any HIP call
+    big = 1 << 36
+    assert f(A, B, None, Y, 1, 1, big, big, big, 1, 1, bf, None) == fk.FK_ERR_UNSUPPORTED
 
 
 def test_attention_validation(L):
