@@ -108,9 +108,38 @@ constexpr int kStagedLds = IO::kVec == 4 ? 4 : 8;     // 128 KiB of LDS
 // The staged kernel addresses a row with 32-bit byte offsets.
 constexpr int64_t kStagedMaxRowBytes = int64_t(1) << 31;
 
+// Compute units of the current device (queried once per device; 0 if the
+// query fails).
+constexpr int kMaxCuDevices = 64;
+std::atomic<int> g_device_cus[kMaxCuDevices];
+
+int device_cus() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxCuDevices) return 0;
+    int n = g_device_cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        g_device_cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 template <class IO>
 hipError_t launch_online(const void* x, void* y, int64_t rows, int64_t cols, int64_t ldx,
                          int64_t ldy, bool vec, hipStream_t s) {
+    constexpr int64_t kStagedChunk = int64_t(kStagedThreads) * kStagedVpl<IO> * IO::kVec;
+    // rows of exactly the chunks that stay on chip (131072 fp32 / 262144
+    // bf16 columns): the rolling kernel, one workgroup per CU (its LDS allows
+    // no second one), each looping over rows
+    const int cus = device_cus();
+    if (vec && cus > 0 && cols == (kStagedReg<IO> + kStagedLds<IO>) * kStagedChunk) {
+        const void* fn = reinterpret_cast<const void*>(
+            &softmax_rolling_kernel<IO, kStagedThreads, kStagedVpl<IO>, kStagedReg<IO>,
+                                    kStagedLds<IO>, kRowNT>);
+        return launch_kernel(fn, rows < cus ? rows : cus, kStagedThreads, s, x, y, rows, cols, ldx,
+                             ldy);
+    }
     if (vec && cols * IO::kBytes < kStagedMaxRowBytes) {
         const void* fn = reinterpret_cast<const void*>(
             &softmax_staged_kernel<IO, kStagedThreads, kStagedVpl<IO>, kStagedReg<IO>,

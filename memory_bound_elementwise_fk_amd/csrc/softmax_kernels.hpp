@@ -654,6 +654,141 @@ __global__ __launch_bounds__(THREADS) void softmax_staged_kernel(
     }
 }
 
+// s_waitcnt immediate: at most n vector memory operations of this wave in
+// flight (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt at
+// their maxima, i.e. not waited for)
+__device__ constexpr int vmcnt_count(int n) {
+    return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+}
+
+// ---------------------------------------------------------- rolling kernel -
+// The staged kernel for rows that stay on chip whole (exactly RREG + RLDS
+// chunks), with a persistent grid (at most one workgroup per CU, each
+// looping over rows) that overlaps a row's second pass with the next row's
+// first: in pass 2, as soon as chunk c of row r is normalised and stored,
+// the same registers (or LDS words) take chunk c of the workgroup's next
+// row, and chunk c - D of that next row (landed by then: a counted wait
+// lets the later D chunks' stores and loads stay in flight) goes into the
+// next row's running (m, l). The staged kernel reads a whole row, reduces
+// it, then writes it, so the GPU alternates between read-only and
+// write-only phases with gaps between them. Each LDS chunk word is written
+// and read by the same lane (the direct loads of a wave fill that wave's
+// own lanes' slots), so no barrier guards their reuse. Same arithmetic, in
+// the same order, as the staged kernel.
+template <class IO, int THREADS, int VPL, int RREG, int RLDS, bool NT>
+__global__ __launch_bounds__(THREADS) void softmax_rolling_kernel(
+    const void* x, void* y, int64_t rows, int64_t cols, int64_t ldx, int64_t ldy) {
+    constexpr int64_t kChunk = int64_t(THREADS) * VPL * IO::kVec;
+    constexpr int kWaves = THREADS / kWave;
+    constexpr int NC = RREG + RLDS;   // chunks per row (cols == NC * kChunk)
+    constexpr int D = 2;              // chunks the next row's pass 1 trails its loads by
+    constexpr int kOps = 2 * VPL;     // memory operations per chunk in pass 2
+    static_assert(NC > D && D == 2 && D * kOps <= 63, "counted waits");
+    __shared__ u32x4 stage[RLDS > 0 ? RLDS : 1][VPL][THREADS];
+    __shared__ float red_m[kWaves];
+    __shared__ float red_l[kWaves];
+
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int wave = tid / kWave;
+    constexpr uint32_t kChunkBytes = uint32_t(kChunk) * IO::kBytes;
+    const uint32_t voff = uint32_t(tid) * 16;
+    const uint32_t row_bytes = uint32_t(cols) * IO::kBytes;
+
+    u32x4 res[RREG][VPL];
+    // chunk c of the lane's words into (m, l)
+    auto update = [&](int c, float& m, float& l) {
+        if (c < RREG) {
+            ml_update_raw<IO, VPL>(res[c], m, l);
+        } else {
+            u32x4 w[VPL];
+#pragma unroll
+            for (int k = 0; k < VPL; ++k) w[k] = stage[c - RREG][k][tid];
+            ml_update_raw<IO, VPL>(w, m, l);
+        }
+    };
+    auto load_chunk = [&](rsrc_t rx, int c) {
+        if (c < RREG) load_chunk_buf<VPL, THREADS, NT>(rx, voff, c * kChunkBytes, res[c]);
+        else load_chunk_lds<VPL, THREADS, NT>(rx, voff, c * kChunkBytes, tid, stage[c - RREG]);
+    };
+
+    // the first row: loaded and reduced on its own
+    float m = kNegInf, l = 0.0f;
+    if (int64_t(blockIdx.x) < rows) {
+        const rsrc_t rx = row_buffer(row_ptr<IO>(x, blockIdx.x, ldx), row_bytes);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) load_chunk(rx, c);
+        __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            update(c, m, l);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+        const int64_t next = row + gridDim.x;
+        const bool more = next < rows;
+        char* yr = row_ptr<IO>(y, row, ldy);
+
+        // merge the lanes' states of this row: the wave (DPP), then the waves
+        wave_ml(m, l);
+        if (lane == 0) {
+            red_m[wave] = m;
+            red_l[wave] = l;
+        }
+        __syncthreads();
+        float M = red_m[0], L = red_l[0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) ml_merge(M, L, red_m[w], red_l[w]);
+
+        // pass 2 of this row, the loads and pass 1 of the next
+        if constexpr (IO::kBytes == 2) {
+#pragma unroll
+            for (int c = 0; c < RREG; ++c)
+#pragma unroll
+                for (int k = 0; k < VPL; ++k) asm volatile("" : "+v"(res[c][k]));
+        }
+        const float r = 1.0f / (L * kSoftmaxScale);
+        const rsrc_t rn = row_buffer(row_ptr<IO>(x, more ? next : row, ldx), row_bytes);
+        m = kNegInf;
+        l = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            if (c < RREG) {
+                normalise_store_global<IO, VPL, THREADS, NT>(yr, voff, c * kChunkBytes, res[c], M, r);
+            } else {
+                u32x4 w[VPL];
+#pragma unroll
+                for (int k = 0; k < VPL; ++k) w[k] = stage[c - RREG][k][tid];
+                normalise_store_global<IO, VPL, THREADS, NT>(yr, voff, c * kChunkBytes, w, M, r);
+                // this lane's words are read before its wave's direct load
+                // replaces them
+                __builtin_amdgcn_s_waitcnt(0xC07F);
+            }
+            if (more) {
+                load_chunk(rn, c);
+                if (c >= D) {
+                    // chunk c - D landed: only the D later chunks' stores and
+                    // loads may be in flight
+                    __builtin_amdgcn_s_waitcnt(vmcnt_count(D * kOps));
+                    update(c - D, m, l);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (more) {  // the last D = 2 chunks of the next row
+            __builtin_amdgcn_s_waitcnt(vmcnt_count(kOps));
+            update(NC - 2, m, l);
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(vmcnt_count(0));
+            update(NC - 1, m, l);
+        }
+        // the next row rewrites red_m / red_l
+        __syncthreads();
+    }
+}
+
 // ------------------------------------------------------------ split kernel -
 // Rows wider than one workgroup's registers, without re-reading HBM: the row
 // is cut into `parts` slices of THREADS*E columns, one workgroup per slice

@@ -278,6 +278,33 @@ def test_online_staged_strided_in_place_and_many_rows(dt):
     check(dt, to_host(xi), ref, "online in place")
 
 
+# Rows of whole chunks that stay on chip run the rolling kernel: a persistent
+# grid (one workgroup per CU) whose pass 2 loads the workgroup's next row
+# into each chunk's registers or LDS words as soon as the current row's
+# chunk is stored. More rows than CUs (several per workgroup, a ragged last
+# round), rows that differ sharply from their neighbours (a NaN row, an all
+# -inf row, a row shifted far up), in place too.
+@pytest.mark.parametrize("dt,chunks", [("f32", 5), ("f32", 12), ("f32", 16), ("bf16", 3),
+                                       ("bf16", 24), ("bf16", 32)])
+def test_online_rolling_many_rows(dt, chunks):
+    cols = chunks * K
+    rows = 701 if chunks * K * 4 <= (1 << 19) else 300
+    x = random_input((rows, cols), dt, 3.0, seed=chunks * 11 + len(dt))
+    if dt == "f32":
+        x[257, 5] = np.nan
+        x[300, :] = -np.inf
+        x[258] += 200.0
+    ref = oracle.softmax_rows(x, threads=T)
+    xt = to_dev(x)
+    full, y = guarded(x.shape, tdtype(dt))
+    fk.fk_softmax_rows_online(xt, y)
+    got = to_host(y)
+    assert guards_intact(full, x.size), "rolling softmax wrote outside its output"
+    check(dt, got, ref, f"rolling {dt} cols={cols} rows={rows}")
+    fk.fk_softmax_rows_online(xt, xt)
+    check(dt, to_host(xt), ref, f"rolling in place {dt} cols={cols}")
+
+
 def test_online_staged_special_rows():
     cols = 18 * K + 5
     x = random_input((5, cols), "f32", 2.0, seed=53)
