@@ -52,7 +52,7 @@ KERNEL_NAMES = {
     "layernorm_gelu": ("layernorm_reg_kernel<fk::IoBF16",),
     "gelu_backward": ("ew2_vec_kernel<fk::IoBF16", "GeluBwdOp"),
     "softmax_backward": ("softmax_bwd_reg_kernel<fk::IoBF16",),
-    "online_c5a": ("softmax_staged_kernel<fk::IoF32",),
+    "online_c5a": ("softmax_rolling_kernel<fk::IoF32",),
 }
 # Next-row kernels in the counter run (bytes per launch: one read of each
 # input, one write of the output; gamma and beta of the LayerNorm once).

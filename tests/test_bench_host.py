@@ -37,7 +37,7 @@ NAMES = {
     "layernorm_gelu": "void fk::layernorm_reg_kernel<fk::IoBF16, 4, 2, true, true, true, 2>(...)",
     "gelu_backward": "void fk::ew2_vec_kernel<fk::IoBF16, 128, true, false, fk::GeluBwdOp>(...)",
     "softmax_backward": "void fk::softmax_bwd_reg_kernel<fk::IoBF16, 2, 4, true, true, 2>(...)",
-    "online_c5a": "void fk::softmax_staged_kernel<fk::IoF32, 512, 4, 12, 4, true>(...)",
+    "online_c5a": "void fk::softmax_rolling_kernel<fk::IoF32, 512, 4, 12, 4, true>(...)",
 }
 
 
