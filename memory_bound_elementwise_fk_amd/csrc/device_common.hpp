@@ -183,9 +183,13 @@ __device__ inline void gelu_tanh_n(float (&v)[N]) {
 #pragma unroll
     for (int j = 0; j < N; ++j) y[j] = v[j] * __builtin_amdgcn_rcpf(1.0f + exp2_raw(t[j]));
     if (__builtin_amdgcn_ballot_w64(tmax > kGeluFarT) != 0) {
+        // every value's far form, then a select: one compare mask live at a
+        // time (a branch per value kept all N masks in SGPR pairs at once)
 #pragma unroll
-        for (int j = 0; j < N; ++j)
-            if (t[j] > kGeluFarT) y[j] = gelu_far(v[j], t[j]);
+        for (int j = 0; j < N; ++j) {
+            const float yf = gelu_far(v[j], t[j]);
+            y[j] = t[j] > kGeluFarT ? yf : y[j];
+        }
     }
 #pragma unroll
     for (int j = 0; j < N; ++j) v[j] = y[j];
