@@ -92,7 +92,7 @@ __device__ inline u32x2 lds_read_tr16(const uint16_t* p) {
     return __builtin_bit_cast(u32x2, r);
 }
 
-// Two waves per SIMD (two workgroups per CU; LDS 64 KiB each): with one, a
+// Two waves per SIMD (two workgroups per CU; LDS 80 KiB each): with one, a
 // wave's MFMA, exponential and LDS phases run back to back and the K/V loads
 // barely overlap them; the second workgroup fills those gaps. The kernel
 // fits in the 256 registers (no AGPRs) this leaves a wave.
@@ -100,7 +100,8 @@ template <class EL, bool WIDE>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attention_fwd_kernel(AttnArgs a) {  // EL: MmaBF16 or MmaF16
     typedef typename EL::frag frag;
-    __shared__ __attribute__((aligned(1024))) uint16_t Ks[2][kAttnBC * kAttnD];
+    // K in three buffers, V in two: 80 KiB, two workgroups fill a CU's LDS
+    __shared__ __attribute__((aligned(1024))) uint16_t Ks[3][kAttnBC * kAttnD];
     __shared__ __attribute__((aligned(1024))) uint16_t Vs[2][kAttnBC * kAttnD];
 
     // One workgroup per (query block, head), numbered level by level with the
@@ -220,22 +221,28 @@ void attention_fwd_kernel(AttnArgs a) {  // EL: MmaBF16 or MmaF16
     auto wave_needs = [&](int64_t kbx) { return !(a.causal && kbx * kAttnBC > q0 + 31); };
 
     // Software pipeline: block kb's softmax (VALU) runs next to block
-    // kb + 1's S^T MFMAs, so K is loaded two blocks ahead and V one: in
-    // iteration kb, K(kb + 2) goes to the K buffer K(kb) left (read for S(kb)
-    // an iteration earlier) and V(kb + 1) to the one V(kb - 1) left. One
-    // barrier per iteration, after every wave's loads have landed.
+    // kb + 1's S^T MFMAs. In iteration kb, V(kb + 1) goes to the V buffer
+    // V(kb - 1) left, then K(kb + 3) to the K buffer K(kb) left (read for
+    // S(kb) an iteration earlier). The next iteration reads K(kb + 2),
+    // loaded an iteration earlier, and V(kb + 1), loaded first in this one,
+    // so the closing wait lets this iteration's K loads stay in flight: K
+    // has two iterations to land, V one. One barrier per iteration.
     issue(false, 0, 0);
     issue(true, 0, 0);
     if (nkb > 1) issue(false, kAttnBC, 1);
+    if (nkb > 2) issue(false, 2 * kAttnBC, 2);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
     f32x16 s_cur[2] = {f32x16{}, f32x16{}};
     if (wave_needs(0)) compute_s(0, s_cur);
-    __syncthreads();  // every wave has read K(0) before K(2) replaces it
+    __syncthreads();  // every wave has read K(0) before K(3) replaces it
+    int kbuf_cur = 0;  // kb % 3
     for (int64_t kb = 0; kb < nkb; ++kb) {
         const int64_t kb0 = kb * kAttnBC;
-        if (kb + 2 < nkb) issue(false, kb0 + 2 * kAttnBC, static_cast<int>(kb & 1));
+        const int kbuf_next = kbuf_cur == 2 ? 0 : kbuf_cur + 1;  // (kb + 1) % 3
         if (kb + 1 < nkb) issue(true, kb0 + kAttnBC, static_cast<int>((kb + 1) & 1));
+        const bool load_k = kb + 3 < nkb;
+        if (load_k) issue(false, kb0 + 3 * kAttnBC, kbuf_cur);
         // S(kb + 1); in the last iteration it reads a stale buffer (valid
         // LDS) and is discarded, which keeps the MFMAs next to the softmax
         f32x16 s_nxt[2];
@@ -254,7 +261,7 @@ void attention_fwd_kernel(AttnArgs a) {  // EL: MmaBF16 or MmaF16
                     }
                 }
             }
-            compute_s(static_cast<int>((kb + 1) & 1), s_nxt);
+            compute_s(kbuf_next, s_nxt);
             float bm = -__builtin_inff();
 #pragma unroll
             for (int t = 0; t < 2; ++t)
@@ -319,15 +326,18 @@ void attention_fwd_kernel(AttnArgs a) {  // EL: MmaBF16 or MmaF16
                 }
             }
         } else {
-            compute_s(static_cast<int>((kb + 1) & 1), s_nxt);
+            compute_s(kbuf_next, s_nxt);
         }
         s_cur[0] = s_nxt[0];
         s_cur[1] = s_nxt[1];
 
-        // this wave's loads have landed; after the barrier every wave's
+        // the loads the next iteration reads have landed (this iteration's
+        // K loads may still be in flight); after the barrier every wave's
         // have, and the buffers read in this iteration are free
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        if (load_k) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kAttnDmaPerWave));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();
+        kbuf_cur = kbuf_next;
     }
 
     // O = acc / l, rounded to bf16; four consecutive dims per 8-byte store
