@@ -13,6 +13,15 @@ int64_t attention_workgroups(int64_t B, int64_t H, int64_t T) {
     return (T + kAttnBQ - 1) / kAttnBQ * B * H;
 }
 
+// heads per group of the kernel's workgroup order: 1 for full attention, up
+// to 4 for causal, a divisor of B H / 8; 0 when B H is not a multiple of 8
+static int64_t attention_head_group(int64_t BH, int causal) {
+    if (BH % 8 != 0) return 0;
+    int64_t g = causal ? 4 : 1;
+    while ((BH / 8) % g != 0) --g;
+    return g;
+}
+
 hipError_t launch_attention_fwd(const void* q, const void* k, const void* v, void* o, int64_t B,
                                 int64_t H, int64_t T, const int64_t* strides, int causal,
                                 Dtype dt, hipStream_t s) {
@@ -30,6 +39,7 @@ hipError_t launch_attention_fwd(const void* q, const void* k, const void* v, voi
     a.ob = strides[9]; a.oh = strides[10]; a.ot = strides[11];
     a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(double(kAttnD)));
     a.causal = causal;
+    a.hgroup = attention_head_group(B * H, causal);
     const int64_t nwg = attention_workgroups(B, H, T);  // <= 2^23, checked by the caller
     void* args[] = {&a};
     // a lane's source offsets within a 64-key block fit 32 bits unless the

@@ -12,9 +12,10 @@
 //
 // MI355X mapping. Each wave owns 32 queries; a workgroup of 4 waves owns
 // 128 queries of one (batch, head) and walks the key blocks of 64 keys,
-// staged through LDS (K and V both as [key][dim], two buffers each, copied
-// by direct global-to-LDS loads: no registers, no ALU; K two blocks ahead,
-// V one, for the software pipeline described at the loop). The wave
+// staged through LDS (K and V both as [key][dim], copied by direct
+// global-to-LDS loads: no registers, no ALU; K in three buffers, loaded
+// three blocks ahead, V in two, one block ahead, for the software pipeline
+// described at the loop). The wave
 // computes the transposed scores S^T = K Q^T with the 32x32x16 bf16 MFMA:
 // K is the A operand (lane l: key l % 32, dims (l / 32) * 8 + e), Q the B
 // operand (query l % 32), held in registers for the whole key loop. In the
@@ -80,6 +81,9 @@ struct AttnArgs {
     int64_t ob, oh, ot;
     float scale_log2;  // log2(e) / sqrt(d)
     int causal;
+    // heads per group of the workgroup order (0: one group of all heads);
+    // > 0 only when B H is a multiple of 8 and (B H / 8) % hgroup == 0
+    int64_t hgroup;
 };
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -104,19 +108,37 @@ void attention_fwd_kernel(AttnArgs a) {  // EL: MmaBF16 or MmaF16
     __shared__ __attribute__((aligned(1024))) uint16_t Ks[3][kAttnBC * kAttnD];
     __shared__ __attribute__((aligned(1024))) uint16_t Vs[2][kAttnBC * kAttnD];
 
-    // One workgroup per (query block, head), numbered level by level with the
-    // heads fastest: level 0 holds every head's longest causal block. The
-    // hardware deals workgroup IDs round-robin to its partitions (8 XCDs,
-    // each split again), so with the heads fastest every partition gets the
-    // same mix of long and short causal blocks, longest first. (Numbered with
-    // the query blocks fastest, a multiple of 32 of them put the same block
-    // position in the same partition every time, and causal attention took as
-    // long as full attention.)
+    // One workgroup per (query block, head). The hardware deals workgroup
+    // IDs round-robin to its partitions: ID mod 8 picks the XCD (each with
+    // its own L2), and each XCD splits its share again. The IDs go level by
+    // level, a level holding one query block of every head in a group, with
+    // the heads fastest: for causal attention level 0 holds the longest
+    // blocks, so every partition gets the same mix of long and short blocks,
+    // longest first. (Numbered with the query blocks fastest, a multiple of
+    // 32 of them put the same block position in the same partition every
+    // time, and causal attention took as long as full attention.) When B H
+    // is a multiple of 8 (hgroup > 0), XCD x takes heads x, x + 8, ... in
+    // groups of hgroup heads: the workgroups running together on an XCD then
+    // share few heads and read each K and V block from its L2 rather than
+    // from HBM. Full attention takes one head per group, so all of a head's
+    // query blocks run together; causal attention groups up to 4 heads,
+    // which keeps most of the longest-first order. Otherwise all heads form
+    // one group.
     const int64_t nqb = (a.T + kAttnBQ - 1) / kAttnBQ;
     const int64_t BH = a.B * a.H;
-    const int64_t lev = int64_t(blockIdx.x) / BH;
-    const int64_t bh = int64_t(blockIdx.x) - lev * BH;
-    const int64_t qblk = a.causal ? nqb - 1 - lev : lev;
+    int64_t bh, qblk;
+    if (a.hgroup > 0) {
+        const int64_t x = blockIdx.x % 8, k = blockIdx.x / 8;  // the XCD's k-th
+        const int64_t per = a.hgroup * nqb;
+        const int64_t grp = k / per, r = k - grp * per;
+        const int64_t lev = r / a.hgroup;
+        bh = (grp * a.hgroup + (r - lev * a.hgroup)) * 8 + x;
+        qblk = a.causal ? nqb - 1 - lev : lev;
+    } else {
+        const int64_t lev = int64_t(blockIdx.x) / BH;
+        bh = int64_t(blockIdx.x) - lev * BH;
+        qblk = a.causal ? nqb - 1 - lev : lev;
+    }
     const int64_t b = bh / a.H, h = bh % a.H;
     const uint16_t* Q = a.q + b * a.qb + h * a.qh;
     const uint16_t* Kg = a.k + b * a.kb + h * a.kh;

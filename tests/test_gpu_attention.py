@@ -80,6 +80,22 @@ def test_attention_shapes(B, H, T, causal, dt):
                {key: ref[key[0], key[1]] for key in rows}, v, f"B{B} H{H} T{T} causal={causal}")
 
 
+# B H a multiple of 8: the workgroups go to the XCDs in groups of heads
+# (1 head for full attention; for causal the largest divisor of B H / 8 up to
+# 4: 1, 2, 3 and 4 below), a different order of the same (head, query block)
+# pairs; every output row is checked, in several query blocks per head.
+@pytest.mark.parametrize("B,H", [(1, 8), (2, 8), (3, 8), (1, 40), (4, 8)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_attention_head_groups(B, H, causal):
+    T = 300
+    q, k, v = qkv(B, H, T, seed=B * 1000 + H)
+    got = run(q, k, v, causal)
+    ref = oracle.attention(q, k, v, causal=causal)
+    rows = {(b, h): np.arange(T) for b in range(B) for h in range(H)}
+    check_rows({key: got[key[0], key[1]] for key in rows},
+               {key: ref[key[0], key[1]] for key in rows}, v, f"B{B} H{H} T{T} causal={causal}")
+
+
 def test_attention_strided_bthd_layout():
     # tensors stored as [B, T, H, d] and viewed as [B, H, T, d]
     B, H, T, d = 2, 4, 300, 128
