@@ -9,8 +9,18 @@ namespace fk {
 
 int64_t attention_head_dim() { return kAttnD; }
 
+// workgroups of the 4-wave shape (the most the kernel is launched with)
 int64_t attention_workgroups(int64_t B, int64_t H, int64_t T) {
-    return (T + kAttnBQ - 1) / kAttnBQ * B * H;
+    return (T + kAttnBQMin - 1) / kAttnBQMin * B * H;
+}
+
+template <int NW>
+static const void* attention_kernel(Dtype dt, bool wide) {
+    return dt == kF16
+               ? (wide ? reinterpret_cast<const void*>(&attention_fwd_kernel<MmaF16, true, NW>)
+                       : reinterpret_cast<const void*>(&attention_fwd_kernel<MmaF16, false, NW>))
+               : (wide ? reinterpret_cast<const void*>(&attention_fwd_kernel<MmaBF16, true, NW>)
+                       : reinterpret_cast<const void*>(&attention_fwd_kernel<MmaBF16, false, NW>));
 }
 
 // heads per group of the kernel's workgroup order: 1 for full attention, up
@@ -40,18 +50,24 @@ hipError_t launch_attention_fwd(const void* q, const void* k, const void* v, voi
     a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(double(kAttnD)));
     a.causal = causal;
     a.hgroup = attention_head_group(B * H, causal);
-    const int64_t nwg = attention_workgroups(B, H, T);  // <= 2^23, checked by the caller
+    // Full attention: 8 waves per workgroup (one per CU) when that still
+    // gives every CU at least two workgroups, else 4 (two per CU). Causal
+    // attention keeps 4: its workgroups' lengths differ, and 256-query
+    // blocks balance worse across the CUs (B4 H32 T1024: 0.068 ms against
+    // 0.058 ms with 4 waves; T4096: the same).
+    const int cus = device_cus();
+    const int64_t nwg8 = (T + kAttnBQ<8> - 1) / kAttnBQ<8> * B * H;
+    const bool w8 = !causal && cus > 0 && nwg8 >= 2 * int64_t(cus);
+    // <= 2^23, checked by the caller
+    const int64_t nwg = w8 ? nwg8 : attention_workgroups(B, H, T);
     void* args[] = {&a};
     // a lane's source offsets within a 64-key block fit 32 bits unless the
     // key strides are enormous (then the 64-bit variant)
     const int64_t lim = (int64_t(1) << 31) - kAttnD;
     const bool wide = a.kt > lim / kAttnBC || a.vt > lim / kAttnBC;
-    const void* fn =
-        dt == kF16 ? (wide ? reinterpret_cast<const void*>(&attention_fwd_kernel<MmaF16, true>)
-                           : reinterpret_cast<const void*>(&attention_fwd_kernel<MmaF16, false>))
-                   : (wide ? reinterpret_cast<const void*>(&attention_fwd_kernel<MmaBF16, true>)
-                           : reinterpret_cast<const void*>(&attention_fwd_kernel<MmaBF16, false>));
-    return hipLaunchKernel(fn, dim3(static_cast<unsigned>(nwg)), dim3(kAttnThreads), args, 0, s);
+    const void* fn = w8 ? attention_kernel<8>(dt, wide) : attention_kernel<4>(dt, wide);
+    return hipLaunchKernel(fn, dim3(static_cast<unsigned>(nwg)), dim3((w8 ? 8 : 4) * kWave), args,
+                           0, s);
 }
 
 }  // namespace fk

@@ -10,8 +10,9 @@
 // the end. As on that page, P is rounded to the input dtype before the
 // P V product. The causal mask keeps key j for query i when j <= i.
 //
-// MI355X mapping. Each wave owns 32 queries; a workgroup of 4 waves owns
-// 128 queries of one (batch, head) and walks the key blocks of 64 keys,
+// MI355X mapping. Each wave owns 32 queries; a workgroup of 8 waves (or 4,
+// for grids too small to fill the GPU) owns 256 (128) queries of one
+// (batch, head) and walks the key blocks of 64 keys,
 // staged through LDS (K and V both as [key][dim], copied by direct
 // global-to-LDS loads: no registers, no ALU; K in three buffers, loaded
 // three blocks ahead, V in two, one block ahead, for the software pipeline
@@ -46,15 +47,14 @@ namespace fk {
 
 constexpr int kAttnD = 128;       // head dimension
 constexpr int kAttnBC = 64;       // keys per block
-constexpr int kAttnWaves = 4;     // waves per workgroup (32 queries each)
-constexpr int kAttnThreads = kAttnWaves * kWave;
-constexpr int kAttnBQ = kAttnWaves * 32;
+constexpr int kAttnWaveQ = 32;    // queries per wave
 constexpr int kAttnRowBytes = kAttnD * 2;                       // one key row of K or V
 constexpr int kAttnBlockBytes = kAttnBC * kAttnRowBytes;        // 16 KiB per operand
-// direct loads per wave, per operand and block (each fills 1 KiB = 4 rows)
-constexpr int kAttnDmaPerWave = kAttnBlockBytes / 1024 / kAttnWaves;
-static_assert(kAttnDmaPerWave * 1024 * kAttnWaves == kAttnBlockBytes, "whole wave loads");
-static_assert(kAttnDmaPerWave == 4, "the staging offsets take a wave's rows as 16 w + 4 j + drow");
+// queries per workgroup of NW waves (4 or 8)
+template <int NW>
+constexpr int kAttnBQ = NW * kAttnWaveQ;
+// the 4-wave shape has the most workgroups: the grid-size limit uses it
+constexpr int kAttnBQMin = kAttnBQ<4>;
 // LDS layout of a block: row r (key) holds its 16 chunks of 16 bytes (8
 // dims each) permuted, chunk c at position c ^ swz(r): K with r % 16 (the
 // S^T fragment reads, 16 consecutive keys of one chunk per 256 bytes, hit
@@ -96,14 +96,21 @@ __device__ inline u32x2 lds_read_tr16(const uint16_t* p) {
     return __builtin_bit_cast(u32x2, r);
 }
 
-// Two waves per SIMD (two workgroups per CU; LDS 80 KiB each): with one, a
-// wave's MFMA, exponential and LDS phases run back to back and the K/V loads
-// barely overlap them; the second workgroup fills those gaps. The kernel
-// fits in the 256 registers (no AGPRs) this leaves a wave.
-template <class EL, bool WIDE>
-__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// Two waves per SIMD: with one, a wave's MFMA, exponential and LDS phases
+// run back to back and the K/V loads barely overlap them; the second wave
+// fills those gaps. The kernel fits in the 256 registers (no AGPRs) this
+// leaves a wave. NW = 8: one workgroup per CU, whose 8 waves share each
+// K/V block (half the direct-load traffic per query of NW = 4, where two
+// workgroups of 4 waves share a CU, LDS 80 KiB each).
+template <class EL, bool WIDE, int NW>
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attention_fwd_kernel(AttnArgs a) {  // EL: MmaBF16 or MmaF16
     typedef typename EL::frag frag;
+    static_assert(NW == 4 || NW == 8, "workgroups of 4 or 8 waves");
+    constexpr int kBQ = kAttnBQ<NW>;
+    // direct loads per wave, per operand and block (each fills 1 KiB = 4 rows)
+    constexpr int kDmaPerWave = kAttnBlockBytes / 1024 / NW;
+    static_assert(kDmaPerWave * 1024 * NW == kAttnBlockBytes, "whole wave loads");
     // K in three buffers, V in two: 80 KiB, two workgroups fill a CU's LDS
     __shared__ __attribute__((aligned(1024))) uint16_t Ks[3][kAttnBC * kAttnD];
     __shared__ __attribute__((aligned(1024))) uint16_t Vs[2][kAttnBC * kAttnD];
@@ -124,7 +131,7 @@ void attention_fwd_kernel(AttnArgs a) {  // EL: MmaBF16 or MmaF16
     // query blocks run together; causal attention groups up to 4 heads,
     // which keeps most of the longest-first order. Otherwise all heads form
     // one group.
-    const int64_t nqb = (a.T + kAttnBQ - 1) / kAttnBQ;
+    const int64_t nqb = (a.T + kBQ - 1) / kBQ;
     const int64_t BH = a.B * a.H;
     int64_t bh, qblk;
     if (a.hgroup > 0) {
@@ -149,7 +156,7 @@ void attention_fwd_kernel(AttnArgs a) {  // EL: MmaBF16 or MmaF16
     const int lane = tid % kWave;
     const int wave = tid / kWave;
     const int g = lane / 32;
-    const int64_t q0 = qblk * kAttnBQ + wave * 32;
+    const int64_t q0 = qblk * kBQ + wave * kAttnWaveQ;
     const int64_t myq = q0 + lane % 32;  // the query of this lane
 
     // Q^T fragments (B operand): query myq, dims kk * 16 + g * 8 + e
@@ -162,22 +169,23 @@ void attention_fwd_kernel(AttnArgs a) {  // EL: MmaBF16 or MmaF16
     }
 
     // key blocks to visit: all, or up to the block's last query when causal
-    const int64_t q_last = (qblk + 1) * kAttnBQ < a.T ? (qblk + 1) * kAttnBQ : a.T;
+    const int64_t q_last = (qblk + 1) * kBQ < a.T ? (qblk + 1) * kBQ : a.T;
     const int64_t kend = a.causal ? q_last : a.T;
     const int64_t nkb = (kend + kAttnBC - 1) / kAttnBC;
 
-    // Staging: wave w's direct load j of a block fills rows 4 (4 w + j) ..
-    // + 3 of K (and of V); lane i writes position i % 16 of row i / 16 of
-    // those, so it fetches the logical chunk at that position. Row
-    // r = 16 w + 4 j + drow has r % 16 = 4 j + drow and r % 4 = drow, so the
-    // lane's source offset within a block is, for K,
-    // (16 w + 4 j) kt + drow kt + ((dpos ^ drow) 8 ^ 32 j) and, for V,
-    // (16 w + 4 j) vt + drow vt + (dpos ^ 4 drow) 8: three lane values for
-    // the eight loads (kept per load they took eight registers, which the
-    // kernel's 256 could not spare). A block wholly inside T adds its first
-    // row; the last partial one clamps rows past T to row T - 1 (valid
-    // memory; those keys are masked, p = 0). LDS addresses are wave-uniform
-    // (scalar).
+    // Staging: wave w's direct load j (of n per operand: 4 for NW = 4, 2
+    // for NW = 8) of a block fills rows 4 u .. 4 u + 3 of K (and of V),
+    // u = n w + j; lane i writes position i % 16 of row i / 16 of those, so
+    // it fetches the logical chunk at that position. Row r = 4 u + drow has
+    // r % 16 = 4 (u % 4) + drow and r % 4 = drow, so the lane's source
+    // offset within a block is, for K, 4 u kt + drow kt +
+    // ((dpos ^ drow) 8 ^ 32 (u % 4)) and, for V, 4 u vt + drow vt +
+    // (dpos ^ 4 drow) 8: three lane values for all the loads, u being
+    // wave-uniform (kept per load the offsets took eight registers, which
+    // the kernel's 256 could not spare). A block wholly inside T adds its
+    // first row; the last partial one clamps rows past T to row T - 1
+    // (valid memory; those keys are masked, p = 0). LDS addresses are
+    // wave-uniform (scalar).
     const int drow = lane / 16, dpos = lane % 16;
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     const uint32_t ks_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((las_ptr)(&Ks[0][0])));
@@ -196,13 +204,14 @@ void attention_fwd_kernel(AttnArgs a) {  // EL: MmaBF16 or MmaF16
         const uint16_t* blk = base + kb0 * st;
         const uint32_t lds = (is_v ? vs_base : ks_base) + static_cast<uint32_t>(buf * kAttnBlockBytes);
 #pragma unroll
-        for (int j = 0; j < kAttnDmaPerWave; ++j) {
-            const uint32_t off = static_cast<uint32_t>((wave_s * kAttnDmaPerWave + j) * 1024);
-            const off_t rows0 = static_cast<off_t>((wave_s * kAttnDmaPerWave + j) * 4 * st);
+        for (int j = 0; j < kDmaPerWave; ++j) {
+            const int u = wave_s * kDmaPerWave + j;
+            const uint32_t off = static_cast<uint32_t>(u * 1024);
+            const off_t rows0 = static_cast<off_t>(u * 4 * st);
             const uint16_t* src =
-                blk + rows0 + (is_v ? v_lane : static_cast<off_t>(k_row + (k_chunk ^ (32 * j))));
+                blk + rows0 + (is_v ? v_lane : static_cast<off_t>(k_row + (k_chunk ^ (32 * (u & 3)))));
             if (!whole) {
-                const int r = (wave * kAttnDmaPerWave + j) * 4 + drow;
+                const int r = (wave * kDmaPerWave + j) * 4 + drow;
                 const int64_t key = kb0 + r < a.T ? kb0 + r : a.T - 1;
                 src = base + key * st + (dpos ^ (is_v ? attn_swz_v(r) : attn_swz_k(r))) * 8;
             }
@@ -356,7 +365,7 @@ void attention_fwd_kernel(AttnArgs a) {  // EL: MmaBF16 or MmaF16
         // the loads the next iteration reads have landed (this iteration's
         // K loads may still be in flight); after the barrier every wave's
         // have, and the buffers read in this iteration are free
-        if (load_k) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kAttnDmaPerWave));
+        if (load_k) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDmaPerWave));
         else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();
         kbuf_cur = kbuf_next;

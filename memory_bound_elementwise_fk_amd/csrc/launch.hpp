@@ -1,12 +1,30 @@
 // launch.hpp -- internal interface between the C ABI layer (api.hip) and the
-// kernel launchers (elementwise.hip, softmax.hip). Arguments reaching these
+// kernel launchers (elementwise.hip, softmax.hip, ...). Arguments reaching these
 // functions have already been validated; they return a hipError_t.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace fk {
+
+// Compute units of the current device (queried once per device; 0 if the
+// query fails).
+inline int device_cus() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
 
 constexpr int kMaxOps = 8;  // equals FK_MAX_OPS of the public header
 

@@ -108,23 +108,6 @@ constexpr int kStagedLds = IO::kVec == 4 ? 4 : 8;     // 128 KiB of LDS
 // The staged kernel addresses a row with 32-bit byte offsets.
 constexpr int64_t kStagedMaxRowBytes = int64_t(1) << 31;
 
-// Compute units of the current device (queried once per device; 0 if the
-// query fails).
-constexpr int kMaxCuDevices = 64;
-std::atomic<int> g_device_cus[kMaxCuDevices];
-
-int device_cus() {
-    int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxCuDevices) return 0;
-    int n = g_device_cus[dev].load(std::memory_order_relaxed);
-    if (n == 0) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            return 0;
-        g_device_cus[dev].store(n, std::memory_order_relaxed);
-    }
-    return n;
-}
-
 template <class IO>
 hipError_t launch_online(const void* x, void* y, int64_t rows, int64_t cols, int64_t ldx,
                          int64_t ldy, bool vec, hipStream_t s) {
