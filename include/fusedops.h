@@ -321,8 +321,8 @@ int fk_linear_gelu(const void* x, const void* w, const void* bias, void* y,
  * the page's kernel rounds P to V's dtype); O rounded once to the dtype.
  * Supported: dtype FK_BF16 or FK_F16 (the pages benchmark fp16), d == 128,
  * 16-byte aligned bases, strides that
- * are multiples of 8, B * H * ceil(T / 128) <= 2^23 (one workgroup per 128
- * queries of one head) -- else FK_ERR_UNSUPPORTED. o must not
+ * are multiples of 8, B * H * ceil(T / 128) <= 2^23 (at most one workgroup
+ * per 128 queries of one head) -- else FK_ERR_UNSUPPORTED. o must not
  * overlap q, k or v (FK_ERR_OVERLAP). B, H or T == 0: nothing to do.
  */
 int fk_attention_fwd(const void* q, const void* k, const void* v, void* o,

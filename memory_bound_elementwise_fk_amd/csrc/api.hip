@@ -310,7 +310,7 @@ int fk_attention_fwd(const void* q, const void* k, const void* v, void* o, int64
     if ((addr & 15u) != 0) return FK_ERR_UNSUPPORTED;
     for (int i = 0; i < 12; ++i)
         if (strides[i] % 8 != 0) return FK_ERR_UNSUPPORTED;
-    // one workgroup per 128 queries of one head, at most 2^23 of them
+    // at most one workgroup per 128 queries of one head, at most 2^23 of them
     if (B > (int64_t(1) << 31) / H || T > (int64_t(1) << 40)) return FK_ERR_UNSUPPORTED;
     if (B * H > fk::kAttnMaxWorkgroups / fk::attention_workgroups(1, 1, T))
         return FK_ERR_UNSUPPORTED;

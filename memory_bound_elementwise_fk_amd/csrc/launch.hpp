@@ -98,8 +98,9 @@ hipError_t launch_attention_fwd(const void* q, const void* k, const void* v, voi
                                 int64_t H, int64_t T, const int64_t* strides, int causal, Dtype dt,
                                 hipStream_t s);
 int64_t attention_head_dim();
-// workgroups of one launch: ceil(T / 128) * B * H (caller keeps it <= 2^23
-// so the grid stays below 2^31 work-items); B * H must not overflow
+// workgroups of a launch in 4-wave workgroups, the most the launcher uses:
+// ceil(T / 128) * B * H (caller keeps it <= 2^23 so the grid stays below
+// 2^31 work-items); B * H must not overflow
 int64_t attention_workgroups(int64_t B, int64_t H, int64_t T);
 constexpr int64_t kAttnMaxWorkgroups = int64_t(1) << 23;
 
