@@ -111,9 +111,10 @@ void attention_fwd_kernel(AttnArgs a) {  // EL: MmaBF16 or MmaF16
     // direct loads per wave, per operand and block (each fills 1 KiB = 4 rows)
     constexpr int kDmaPerWave = kAttnBlockBytes / 1024 / NW;
     static_assert(kDmaPerWave * 1024 * NW == kAttnBlockBytes, "whole wave loads");
-    // K in three buffers, V in two: 80 KiB, two workgroups fill a CU's LDS
-    __shared__ __attribute__((aligned(1024))) uint16_t Ks[3][kAttnBC * kAttnD];
-    __shared__ __attribute__((aligned(1024))) uint16_t Vs[2][kAttnBC * kAttnD];
+    // K in three buffers (kv[0..2]), V in two (kv[3..4]): 80 KiB, two 4-wave
+    // workgroups fill a CU's LDS; after the key loop, the output's staging
+    constexpr int kKBuf0 = 0, kVBuf0 = 3;
+    __shared__ __attribute__((aligned(1024))) uint16_t kv[5][kAttnBC * kAttnD];
 
     // One workgroup per (query block, head). The hardware deals workgroup
     // IDs round-robin to its partitions: ID mod 8 picks the XCD (each with
@@ -188,8 +189,8 @@ void attention_fwd_kernel(AttnArgs a) {  // EL: MmaBF16 or MmaF16
     // wave-uniform (scalar).
     const int drow = lane / 16, dpos = lane % 16;
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-    const uint32_t ks_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((las_ptr)(&Ks[0][0])));
-    const uint32_t vs_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((las_ptr)(&Vs[0][0])));
+    const uint32_t ks_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((las_ptr)(&kv[kKBuf0][0])));
+    const uint32_t vs_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((las_ptr)(&kv[kVBuf0][0])));
     // element offsets within a block: 32-bit unless 64 rows of a stride
     // exceed 2^31 elements (WIDE, chosen on the host)
     typedef typename std::conditional<WIDE, int64_t, int32_t>::type off_t;
@@ -238,7 +239,7 @@ void attention_fwd_kernel(AttnArgs a) {  // EL: MmaBF16 or MmaF16
     auto compute_s = [&](int kbuf, f32x16 (&s)[2]) {
         s[0] = f32x16{};
         s[1] = f32x16{};
-        const uint16_t* kbase = &Ks[kbuf][kr * kAttnD];
+        const uint16_t* kbase = &kv[kKBuf0 + kbuf][kr * kAttnD];
 #pragma unroll
         for (int kk = 0; kk < kAttnD / 16; ++kk)
 #pragma unroll
@@ -341,7 +342,7 @@ void attention_fwd_kernel(AttnArgs a) {  // EL: MmaBF16 or MmaF16
             // transposing reads; key chunks outer, the four independent
             // d-tiles inner). Rows k0 + e have e = (k0 + e) % 4, so their
             // swizzle is 4 e.
-            const uint16_t* vbuf = &Vs[kb & 1][0];
+            const uint16_t* vbuf = &kv[kVBuf0 + (kb & 1)][0];
 #pragma unroll
             for (int ch = 0; ch < 4; ++ch) {
                 const int k0 = ch * 16 + 4 * g;
@@ -371,19 +372,42 @@ void attention_fwd_kernel(AttnArgs a) {  // EL: MmaBF16 or MmaF16
         kbuf_cur = kbuf_next;
     }
 
-    // O = acc / l, rounded to bf16; four consecutive dims per 8-byte store
-    if (myq < a.T) {
+    // O = acc / l, rounded to bf16. A lane holds one query's row (four
+    // consecutive dims per (dt, v4)), so stores straight from the registers
+    // would touch 32 rows per instruction; the wave stages its 32 rows in
+    // LDS (rows padded to 272 bytes: the 8-byte writes of 32 rows spread
+    // over the banks) and stores whole 256-byte rows, 16 lanes per row,
+    // 16 bytes per lane. The key loop's closing barrier has freed the K/V
+    // buffers (8 waves x 8.5 KiB fit in their 80 KiB).
+    {
+        constexpr int kRow = kAttnD + 8;  // staged row, elements
+        static_assert(NW * kAttnWaveQ * kRow * 2 <= int(sizeof(kv)), "output staging fits");
+        // (the lane index made opaque here: the addresses below are then
+        // computed after the loop rather than kept in registers across it)
+        int lane_e = lane;
+        asm volatile("" : "+v"(lane_e));
+        uint16_t* stage = &kv[0][0] + wave * (kAttnWaveQ * kRow);
         const float r = 1.0f / l;
-        uint16_t* orow = O + myq * a.ot;
+        const int q = lane_e % 32;
 #pragma unroll
         for (int dt = 0; dt < kAttnD / 32; ++dt) {
 #pragma unroll
             for (int v4 = 0; v4 < 4; ++v4) {
                 const int d = dt * 32 + v4 * 8 + g * 4;
-                uint32_t w0 = EL::cvt2(acc[dt][v4 * 4 + 0] * r, acc[dt][v4 * 4 + 1] * r);
-                uint32_t w1 = EL::cvt2(acc[dt][v4 * 4 + 2] * r, acc[dt][v4 * 4 + 3] * r);
-                *reinterpret_cast<uint64_t*>(orow + d) = uint64_t(w0) | (uint64_t(w1) << 32);
+                const uint32_t w0 = EL::cvt2(acc[dt][v4 * 4 + 0] * r, acc[dt][v4 * 4 + 1] * r);
+                const uint32_t w1 = EL::cvt2(acc[dt][v4 * 4 + 2] * r, acc[dt][v4 * 4 + 3] * r);
+                *reinterpret_cast<uint64_t*>(stage + q * kRow + d) = uint64_t(w0) | (uint64_t(w1) << 32);
             }
+        }
+        // the wave reads rows other lanes wrote
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int i = 0; i < kAttnWaveQ / 4; ++i) {
+            const int row = i * 4 + lane_e / 16, c = lane_e % 16;
+            const u32x4 val = *reinterpret_cast<const u32x4*>(stage + row * kRow + c * 8);
+            if (q0 + row < a.T) *reinterpret_cast<u32x4*>(O + (q0 + row) * a.ot + c * 8) = val;
         }
     }
 }
