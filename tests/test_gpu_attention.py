@@ -130,15 +130,15 @@ def test_attention_benchmark_grid_sampled(T, dt):
         check_rows(got, ref, v, f"{dt} T={T} causal={causal}")
 
 
-# B H T large enough that the launcher takes workgroups of 8 waves for full
-# attention (256 queries, one per CU: 512 of them here, at least two per CU
-# of a 256-CU MI355X; causal attention keeps 4 waves); T = 300 leaves the
-# second query block ragged (44 queries) and the last key block partial.
-# Every row of six heads is checked.
+# B H T large enough that the launcher takes workgroups of 8 waves (256
+# queries, one per CU: 2048 of them here, at least the two per CU that full
+# attention needs and the eight that causal attention needs on a 256-CU
+# MI355X); T = 300 leaves the second query block ragged (44 queries) and the
+# last key block partial. Every row of six heads is checked.
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("dt", ["bf16", "fp16"])
 def test_attention_eight_wave_workgroups(causal, dt):
-    B, H, T = 8, 32, 300
+    B, H, T = 8, 128, 300
     q, k, v = qkv(B, H, T, seed=31 + causal, dt=dt)
     o = fk.attention_fwd(to_dev(q), to_dev(k), to_dev(v), causal=causal)
     rng = np.random.default_rng(7 + causal)
@@ -214,12 +214,12 @@ def test_attention_wide_key_strides(causal):
 
 @pytest.mark.parametrize("causal", [False, True])
 def test_attention_wide_key_strides_eight_waves(causal):
-    # The 64-bit load-offset variant in the 8-wave shape (full attention;
-    # causal keeps 4 waves): every one of the 512 heads reads the same K and
-    # V rows, 2^25 + 8 elements apart (head and batch strides 0), so 512
-    # workgroups fit in about 4.4 GB per operand; each head has its own
-    # queries.
-    B, H, T, d = 2, 256, 66, 128
+    # The 64-bit load-offset variant in the 8-wave shape: every one of the
+    # 2048 heads reads the same K and V rows, 2^25 + 8 elements apart (head
+    # and batch strides 0), so 2048 workgroups (enough for 8 waves, full or
+    # causal, on a 256-CU MI355X) fit in about 4.4 GB per operand; each head
+    # has its own queries.
+    B, H, T, d = 2, 1024, 66, 128
     stride = (1 << 25) + 8
     q, _, _ = qkv(B, H, T, seed=29)
     _, k1, v1 = qkv(1, 1, T, seed=30)
@@ -234,7 +234,7 @@ def test_attention_wide_key_strides_eight_waves(causal):
     fk.fk_attention_fwd(to_dev(q), views[0], views[1], o, causal=causal)
     kb = np.broadcast_to(k1, (B, H, T, d))
     vb = np.broadcast_to(v1, (B, H, T, d))
-    picks = {(0, 0): np.arange(T), (1, 255): np.arange(T), (1, 77): np.arange(T)}
+    picks = {(0, 0): np.arange(T), (1, 1023): np.arange(T), (1, 77): np.arange(T)}
     ref = oracle.attention(q, kb, vb, causal=causal, rows=picks)
     got = {key: to_host(o[key[0], key[1]]) for key in picks}
     check_rows(got, ref, vb, f"wide strides, 8 waves, causal={causal}")
