@@ -275,8 +275,9 @@ void attention_fwd_kernel(AttnArgs a) {  // EL: MmaBF16 or MmaF16
         if (kb + 1 < nkb) issue(true, kb0 + kAttnBC, static_cast<int>((kb + 1) & 1));
         const bool load_k = kb + 3 < nkb;
         if (load_k) issue(false, kb0 + 3 * kAttnBC, kbuf_cur);
-        // S(kb + 1); in the last iteration it reads a stale buffer (valid
-        // LDS) and is discarded, which keeps the MFMAs next to the softmax
+        // S(kb + 1); in the last iteration, or in a causal wave's last
+        // block, it reads a stale or unneeded buffer (valid LDS) and is
+        // discarded, which keeps the MFMAs next to the softmax
         f32x16 s_nxt[2];
         if (wave_needs(kb)) {
             f32x16 (&s)[2] = s_cur;
@@ -357,11 +358,11 @@ void attention_fwd_kernel(AttnArgs a) {  // EL: MmaBF16 or MmaF16
                     acc[dt] = EL::mfma(__builtin_bit_cast(frag, w), pf[ch], acc[dt]);
                 }
             }
-        } else {
-            compute_s(kbuf_next, s_nxt);
+            s_cur[0] = s_nxt[0];
+            s_cur[1] = s_nxt[1];
         }
-        s_cur[0] = s_nxt[0];
-        s_cur[1] = s_nxt[1];
+        // (a wave past its queries' last block, causal, computes nothing:
+        // the later blocks lie past them too)
 
         // the loads the next iteration reads have landed (this iteration's
         // K loads may still be in flight); after the barrier every wave's
