@@ -149,6 +149,22 @@ def test_attention_eight_wave_workgroups(causal, dt):
     check_rows(got, ref, v, f"8-wave {dt} causal={causal}")
 
 
+# 8-wave workgroups with B H not a multiple of 8 (one group of all heads,
+# level by level): 1030 heads x 2 query blocks of 256 = 2060 workgroups, at
+# least eight per CU of a 256-CU MI355X, so causal attention takes 8 waves
+# as well; every row of five heads, the last one included, is checked.
+@pytest.mark.parametrize("causal", [True, False])
+def test_attention_eight_wave_workgroups_ungrouped_heads(causal):
+    B, H, T = 2, 515, 300
+    q, k, v = qkv(B, H, T, seed=37 + causal)
+    o = fk.attention_fwd(to_dev(q), to_dev(k), to_dev(v), causal=causal)
+    picks = {(0, 0): np.arange(T), (0, 514): np.arange(T), (1, 0): np.arange(T),
+             (1, 257): np.arange(T), (1, 514): np.arange(T)}
+    ref = oracle.attention(q, k, v, causal=causal, rows=picks)
+    got = {key: to_host(o[key[0], key[1]]) for key in picks}
+    check_rows(got, ref, v, f"8-wave, B H = 1030, causal={causal}")
+
+
 def test_attention_closed_forms():
     # Q = 0: uniform weights, the causal output is the prefix mean of V
     B, H, T = 1, 1, 300
