@@ -51,14 +51,15 @@ hipError_t launch_attention_fwd(const void* q, const void* k, const void* v, voi
     a.causal = causal;
     a.hgroup = attention_head_group(B * H, causal);
     // 8 waves per workgroup (one per CU) when that still gives every CU at
-    // least two workgroups (full attention) or eight (causal), else 4 (two
-    // per CU). Causal workgroups differ in length, and 256-query blocks
-    // balance worse across the CUs unless there are many rounds of them
-    // (B4 H32: T1024 0.064 ms against 0.055 ms with 4 waves, T2048 0.165
-    // against 0.163 ms, T4096 0.589-0.606 against 0.608-0.613 ms).
+    // least four workgroups, else 4 (two per CU). Measured on B4 H32 (8 / 4
+    // waves): full T1024 0.086 / 0.084 ms, T2048 0.269 / 0.281 ms, T4096
+    // 1.027 / 1.075 ms; causal T1024 0.065 / 0.059 ms, T2048 0.163 / 0.168
+    // ms, T4096 0.575 / 0.595 ms. With fewer rounds the 256-query
+    // workgroups (causal: of different lengths) balance worse across the
+    // CUs than 128-query ones.
     const int cus = device_cus();
     const int64_t nwg8 = (T + kAttnBQ<8> - 1) / kAttnBQ<8> * B * H;
-    const bool w8 = cus > 0 && nwg8 >= (causal ? 8 : 2) * int64_t(cus);
+    const bool w8 = cus > 0 && nwg8 >= 4 * int64_t(cus);
     // <= 2^23, checked by the caller
     const int64_t nwg = w8 ? nwg8 : attention_workgroups(B, H, T);
     void* args[] = {&a};

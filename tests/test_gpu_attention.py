@@ -131,9 +131,8 @@ def test_attention_benchmark_grid_sampled(T, dt):
 
 
 # B H T large enough that the launcher takes workgroups of 8 waves (256
-# queries, one per CU: 2048 of them here, at least the two per CU that full
-# attention needs and the eight that causal attention needs on a 256-CU
-# MI355X); T = 300 leaves the second query block ragged (44 queries) and the
+# queries, one per CU: 2048 of them here, at least the four per CU that it
+# needs for 8 waves on a 256-CU MI355X); T = 300 leaves the second query block ragged (44 queries) and the
 # last key block partial. Every row of six heads is checked.
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("dt", ["bf16", "fp16"])
@@ -151,8 +150,8 @@ def test_attention_eight_wave_workgroups(causal, dt):
 
 # 8-wave workgroups with B H not a multiple of 8 (one group of all heads,
 # level by level): 1030 heads x 2 query blocks of 256 = 2060 workgroups, at
-# least eight per CU of a 256-CU MI355X, so causal attention takes 8 waves
-# as well; every row of five heads, the last one included, is checked.
+# least four per CU of a 256-CU MI355X, so both masks take 8 waves; every
+# row of five heads, the last one included, is checked.
 @pytest.mark.parametrize("causal", [True, False])
 def test_attention_eight_wave_workgroups_ungrouped_heads(causal):
     B, H, T = 2, 515, 300
