@@ -21,8 +21,8 @@
 //    step separates the buffers. LDS rows are padded by 16 bytes so the
 //    16-byte fragment reads of 32 consecutive rows do not pile onto the
 //    same banks.
-//  * linear_gelu_dtl_kernel (K a multiple of 32): operands go straight from
-//    global memory into a ring of LDS stages (described at the kernel).
+//  * linear_gelu_dtl_kernel (K a multiple of 32 or 64): operands go straight
+//    from global memory into a ring of LDS stages (described at the kernel).
 // Both multiply in the same k order, so their outputs are bitwise equal.
 //
 // MFMA 32x32x16 bf16 operand layout (checked on the device): lane l supplies
@@ -219,28 +219,41 @@ void linear_gelu_kernel(
 // stages, loaded kStages - 1 K steps ahead; each step waits for its own
 // stage with a counted wait on the loads still in flight, then one barrier.
 //
-// LDS layout of a stage: A rows then B rows, each row BK bf16 = 4 chunks of
-// 16 bytes, chunk c of row r stored at chunk position c ^ ((r >> 2) & 3) of
-// the row. The MFMA fragment reads (32 consecutive rows, one chunk) then
-// spread over all 16 bank groups of 16 bytes. A wave's direct load fills 16
-// rows (1 KiB), so lane i fetches row i / 4, chunk (i & 3) ^ ((i >> 4) & 3).
+// LDS layout of a stage: A rows then B rows, each row BK bf16 = BK / 8
+// chunks of 16 bytes, chunk c of row r stored at chunk position c ^ swz(r):
+// (r >> 2) & 3 for 64-byte rows (BK 32), (r >> 1) & 7 for 128-byte rows
+// (BK 64). The MFMA fragment reads (16 consecutive rows, one chunk, per
+// quarter wave) then spread over all 16 bank groups of 16 bytes. A wave's
+// direct load fills 1 KiB, 1024 / (2 BK) rows, so lane i fetches row
+// i / (BK / 8), chunk (i % (BK / 8)) ^ swz(row).
+//
+// K steps of 64 when K allows: a load then covers whole 128-byte lines (8
+// rows), where K steps of 32 request half lines (16 rows of 64 bytes), twice
+// the requests to L2 for the same bytes; with two stages of 64 KiB each K
+// step's loads have the previous step to land (8192 x 16384 x 4096: 1.031
+// -> 0.992 ms, bitwise the same outputs: same k order).
 //
 // Rows past M or N load row M - 1 or N - 1 instead (valid memory; those
 // outputs are never stored). K must be a multiple of BK.
-template <int BM_, int BN_, int WM_, int WN_, int OCC_, int STAGES_>
+template <int BM_, int BN_, int WM_, int WN_, int OCC_, int STAGES_, int BK_ = 32>
 struct DtlShape {
-    static constexpr int BM = BM_, BN = BN_, BK = 32, WM = WM_, WN = WN_;
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
     static constexpr int kOcc = OCC_, kStages = STAGES_;
     static constexpr int kWavesM = BM / WM, kWavesN = BN / WN;
     static constexpr int kWaves = kWavesM * kWavesN;
     static constexpr int kThreads = kWaves * kWave;
     static constexpr int kTM = WM / 32, kTN = WN / 32;
-    static constexpr int kRowBytes = BK * 2;                      // 64
+    static constexpr int kRowBytes = BK * 2;                      // 64 or 128
+    static constexpr int kChunks = BK / 8;                        // 16-byte chunks per row
+    static constexpr int kRowsPerLoad = 1024 / kRowBytes;         // rows of one 1 KiB wave load
     static constexpr int kStageBytes = (BM + BN) * kRowBytes;
-    static constexpr int kLoadsPerWave = (BM + BN) / 16 / kWaves;  // 1 KiB wave loads per step
-    static_assert((BM + BN) % (16 * kWaves) == 0, "whole wave loads");
+    static constexpr int kLoadsPerWave = (BM + BN) / kRowsPerLoad / kWaves;  // per step
+    static_assert(BK == 32 || BK == 64, "K steps of 32 or 64");
+    static_assert((BM + BN) % (kRowsPerLoad * kWaves) == 0, "whole wave loads");
     static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "tiles");
     static_assert(kStages >= 2 && kStages * kStageBytes <= 160 * 1024, "LDS");
+    // chunk position of logical chunk c of stage row r: c ^ swz(r)
+    __device__ static constexpr int swz(int r) { return BK == 32 ? ((r >> 2) & 3) : ((r >> 1) & 7); }
 };
 
 typedef __attribute__((address_space(3))) void* las_ptr;
@@ -290,15 +303,17 @@ void linear_gelu_dtl_kernel(const uint16_t* __restrict__ X, const uint16_t* __re
     const int wave = tid / kWave;
     const int wm = wave / S::kWavesN, wn = wave % S::kWavesN;
 
-    // this lane's source rows for its wave's loads (row groups of 16 of the
-    // stage: A rows 0 .. BM - 1, then B rows), with the chunk swizzle
-    const int lrow = lane / 4;
-    const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);
+    // this lane's source rows for its wave's loads (row groups of
+    // kRowsPerLoad of the stage: A rows 0 .. BM - 1, then B rows), with the
+    // chunk swizzle
+    const int lrow = lane / S::kChunks;
+    const int lpos = lane % S::kChunks;
     const uint16_t* src[S::kLoadsPerWave];
 #pragma unroll
     for (int j = 0; j < S::kLoadsPerWave; ++j) {
-        const int grp = wave * S::kLoadsPerWave + j;  // 16-row group of the stage
-        const int r = grp * 16 + lrow;
+        const int grp = wave * S::kLoadsPerWave + j;  // row group of the stage
+        const int r = grp * S::kRowsPerLoad + lrow;
+        const int lchunk = lpos ^ S::swz(r);
         if (r < S::BM) {
             const int64_t row = m0 + r < M ? m0 + r : M - 1;
             src[j] = X + row * ldx + lchunk * 8;
@@ -359,13 +374,13 @@ void linear_gelu_dtl_kernel(const uint16_t* __restrict__ X, const uint16_t* __re
             for (int i = 0; i < S::kTM; ++i) {
                 const int r = wm * S::WM + i * 32 + frow;
                 af[i] = *reinterpret_cast<const typename EL::frag*>(stage + r * S::kRowBytes +
-                                                         ((c ^ ((r >> 2) & 3)) << 4));
+                                                         ((c ^ S::swz(r)) << 4));
             }
 #pragma unroll
             for (int j = 0; j < S::kTN; ++j) {
                 const int r = S::BM + wn * S::WN + j * 32 + frow;
                 bf[j] = *reinterpret_cast<const typename EL::frag*>(stage + r * S::kRowBytes +
-                                                         ((c ^ ((r >> 2) & 3)) << 4));
+                                                         ((c ^ S::swz(r)) << 4));
             }
 #pragma unroll
             for (int i = 0; i < S::kTM; ++i)

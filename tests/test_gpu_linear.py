@@ -67,7 +67,8 @@ def check(got, x, w, b, gelu, what, rows=None):
     assert within >= 0.99, f"{what}: only {within:.4f} of outputs within one bf16 ulp"
 
 
-# K % 32 == 0 takes the direct-to-LDS kernel (rows past M or N clamped),
+# K % 64 == 0 takes the direct-to-LDS kernel with K steps of 64, other
+# K % 32 == 0 the one with K steps of 32 (rows past M or N clamped in both),
 # other K the register-staged one
 @pytest.mark.parametrize("M,N,K", [(1, 1, 8), (7, 13, 24), (300, 200, 392), (256, 256, 64),
                                    (257, 511, 520), (512, 768, 1024), (1000, 300, 8),
@@ -107,7 +108,7 @@ def test_linear_without_bias_and_k_zero():
     assert np.array_equal(to_host(ye), np.broadcast_to(oracle.gelu_tanh(b), (5, 70)))
 
 
-@pytest.mark.parametrize("K", [136, 160, 192])  # register-staged / direct-to-LDS kernel
+@pytest.mark.parametrize("K", [136, 160, 192])  # register-staged / direct (32) / direct (64)
 def test_linear_strided_operands(K):
     M, N = 300, 260
     x, w, b = operands(M, N, K, seed=5)
