@@ -272,7 +272,7 @@ int fk_linear_gelu(const void* x, const void* w, const void* bias, void* y, int6
     if (ldy < N || (K > 0 && (ldx < K || ldw < K))) return FK_ERR_INVALID_ARG;
     if (dtype == FK_F32) return FK_ERR_UNSUPPORTED;
     // x and w are read only when K > 0 (K == 0 gives GELU(bias))
-    // the kernels count K steps of 32 in 32 bits
+    // the kernels count K steps (of 32 or more) in 32 bits
     if (K >= (int64_t(1) << 36)) return FK_ERR_UNSUPPORTED;
     if (K > 0 && (K % 8 != 0 || ldx % 8 != 0 || ldw % 8 != 0 ||
                   ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w)) & 15u) != 0))
