@@ -14,12 +14,14 @@
 // for grids too small to fill the GPU) owns 256 (128) queries of one
 // (batch, head) and walks the key blocks of 64 keys,
 // staged through LDS (K and V both as [key][dim], copied by direct
-// global-to-LDS loads: no registers, no ALU; K in three buffers, loaded
-// three blocks ahead, V in two, one block ahead, for the software pipeline
-// described at the loop). The wave
+// global-to-LDS loads: no registers, no ALU; K in three buffers, each
+// block loaded two iterations before its scores are computed, V in two, one
+// iteration before its P V product, for the software pipeline described at
+// the loop). The wave
 // computes the transposed scores S^T = K Q^T with the 32x32x16 bf16 MFMA:
 // K is the A operand (lane l: key l % 32, dims (l / 32) * 8 + e), Q the B
-// operand (query l % 32), held in registers for the whole key loop. In the
+// operand (query l % 32), staged through LDS once and then held in
+// registers for the whole key loop. In the
 // accumulator layout of S^T every lane holds one query (l % 32) and 16 of
 // the 32 keys of a tile (lane l ^ 32 holds the other 16), so the row max and
 // sum of a query are a lane-local reduction plus one exchange with lane
