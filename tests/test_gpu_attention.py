@@ -148,6 +148,22 @@ def test_attention_eight_wave_workgroups(causal, dt):
     check_rows(got, ref, v, f"8-wave {dt} causal={causal}")
 
 
+# 8-wave workgroups over 1, 2, 3 and 4 key blocks (T = 40, 100, 150, 200:
+# one query block each, 1024 workgroups, four per CU): the prologue's
+# counted waits and the first iterations' loads differ with the number of
+# key blocks. Every row of three heads, the last one included.
+@pytest.mark.parametrize("T", [40, 100, 150, 200])
+@pytest.mark.parametrize("causal", [True, False])
+def test_attention_eight_wave_few_key_blocks(T, causal):
+    B, H = 8, 128
+    q, k, v = qkv(B, H, T, seed=41 + T + causal)
+    o = fk.attention_fwd(to_dev(q), to_dev(k), to_dev(v), causal=causal)
+    picks = {(0, 0): np.arange(T), (3, 77): np.arange(T), (7, 127): np.arange(T)}
+    ref = oracle.attention(q, k, v, causal=causal, rows=picks)
+    got = {key: to_host(o[key[0], key[1]]) for key in picks}
+    check_rows(got, ref, v, f"8-wave T={T} causal={causal}")
+
+
 # 8-wave workgroups with B H not a multiple of 8 (one group of all heads,
 # level by level): 1030 heads x 2 query blocks of 256 = 2060 workgroups, at
 # least four per CU of a 256-CU MI355X, so both masks take 8 waves; every
